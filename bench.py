@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention forward on one MI355X.
+
+One step = one launch of the whole forward (attn_fwd: scores, online softmax,
+output contraction, epilogue) over the workload's seeded synthetic inputs,
+already resident in HBM.  W warm-up steps, then K timed steps on torch's
+current stream, bracketed by torch.cuda.synchronize().  Prints ONE JSON line.
+
+value       : algorithmic TFLOP/s of the step, FLOPs counted as the pages count
+              them: 4 * Nq * Nk * d per head, halved under the causal mask
+              (FlashAttention-4 (papercache summary), experimental setup).
+roofline    : the forward kernel against the dense bf16 MFMA peak of MI355X
+              (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU); its
+              duration is the mean of per-launch HIP events recorded on the
+              launch stream inside the timed region.
+cpu_baseline: the CPU oracle as it stands, timed on this host on a bounded
+              sample of heads of the same workload (heads are independent and
+              equal in cost, so the rate is the workload's rate).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from exact_attention_18_amd import attn, inputs
+
+PEAK_BF16_TFLOPS = 2516.6
+METRIC = "attn fwd TFLOP/s bf16 hd128 causal N=8192 + % of MFMA bf16 peak"
+
+
+def algorithmic_flops(w: inputs.Workload, x) -> float:
+    if w.varlen:
+        lens = x["lengths"].to(torch.float64)
+        per = (4.0 * lens * lens * w.d).sum().item()
+        f = per * w.Hq
+    else:
+        nk = (torch.full((w.B,), float(w.N), dtype=torch.float64) if x["seqlens_k"] is None
+              else x["seqlens_k"].to(torch.float64))
+        f = (4.0 * w.N * nk * w.d).sum().item() * w.Hq
+    return f / 2.0 if w.causal else f
+
+
+def make_step(w, x, dev):
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    out = torch.empty_like(q)
+    if w.varlen:
+        cu = x["cu_seqlens_q"].to(dev)
+        ms = x["max_seqlen"]
+        lse = torch.empty((w.Hq, q.shape[0]), dtype=torch.float32, device=dev)
+
+        def step():
+            attn.attn_fwd_varlen(q, k, v, cu, cu, ms, ms, w.scale, w.causal, out=out, lse=lse)
+    else:
+        sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            attn.attn_fwd(q, k, v, w.scale, w.causal, sl, out=out, lse=lse)
+    return step
+
+
+def cpu_baseline(w, x, target_s: float):
+    """Time the oracle on whole heads until about target_s seconds have passed."""
+    import oracle
+    from oracle.attention import default_workers
+
+    workers = default_workers()
+    if w.varlen:
+        return None
+    q = x["q"].float().numpy()
+    k = x["k"].float().numpy()
+    v = x["v"].float().numpy()
+    sl = None if x["seqlens_k"] is None else x["seqlens_k"].numpy()
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    rng = np.random.default_rng(w.seed)
+    rng.shuffle(heads)
+    done, t_total, pos = 0, 0.0, 0
+    while pos < len(heads) and t_total < target_s:
+        chunk = heads[pos:pos + workers]
+        t0 = time.perf_counter()
+        oracle.attention_forward(q, k, v, w.scale, w.causal, sl, workers=workers, heads=chunk)
+        t_total += time.perf_counter() - t0
+        done += len(chunk)
+        pos += len(chunk)
+    flops_per_head = algorithmic_flops(w, x) / (w.B * w.Hq)
+    return {"value": flops_per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs of {w.name}, fp64 NumPy with S "
+                      f"and P materialised, {workers} threads, {t_total:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the forward "
+              f"shards over (batch, KV head) with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    x = inputs.workload_inputs(w)
+    flops = algorithmic_flops(w, x)
+    step = make_step(w, x, dev)
+    attn.load_library()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        ev_s[i].record()
+        step()
+        ev_e[i].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]))
+    print(f"[bench] {K} steps, {ms_step:.4f} ms/step, kernel {kernel_ms:.4f} ms", file=sys.stderr,
+          flush=True)
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+    cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+           "causal": w.causal, "q_mult": w.q_mult, "algorithmic_flop": flops,
+           "parallelism": "single GPU"}
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1) bf16)",
+        "config": cfg,
+        "pct_of_mfma_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms": round(kernel_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

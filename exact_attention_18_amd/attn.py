@@ -1,0 +1,187 @@
+"""Thin ctypes binding over libattn.so (argument marshalling only).
+
+Every step of the forward runs in the HIP kernels of libattn.so; this module
+checks tensor dtypes, devices, shapes and contiguity, allocates the outputs
+with PyTorch when the caller does not pass them, and forwards raw device
+pointers and torch's current HIP stream to the C ABI declared in
+``include/attn.h``.  There is no fallback: if the library is missing or a call
+returns an error, a ``RuntimeError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+# attn_status codes (include/attn.h)
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_HEAD_DIM = -2
+ATTN_ERR_HEADS = -3
+ATTN_ERR_SIZE = -4
+ATTN_ERR_LAUNCH = -5
+ATTN_ERR_ALIGN = -6
+ATTN_ERR_TOO_LARGE = -7
+
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_strerror", "attn_last_hip_error", "attn_version")
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Open libattn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                    i32, vp]
+    lib.attn_fwd_varlen.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = i32
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != ATTN_OK:
+        lib = load_library()
+        msg = f"{what}: {strerror(rc)} (status {rc})"
+        if rc == ATTN_ERR_LAUNCH:
+            msg += f", hipError {lib.attn_last_hip_error()}"
+        raise RuntimeError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+             causal: bool = False, seqlens_k: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O, LSE = attention forward of bf16 q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d].
+
+    Returns O bf16 [B,Nq,Hq,d] and LSE fp32 [B,Hq,Nq] (natural log).  Launches
+    on torch's current stream of q's device and does not synchronise.
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d] of equal shape")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("q and k disagree on batch or head dim")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if seqlens_k is not None:
+        _need(seqlens_k, "seqlens_k", torch.int32, dev)
+        if seqlens_k.shape != (B,):
+            raise ValueError("seqlens_k must have shape [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    else:
+        _need(lse, "lse", torch.float32, dev)
+        if lse.shape != (B, Hq, Nq):
+            raise ValueError("lse must have shape [B,Hq,Nq]")
+    rc = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                      float(scale), int(bool(causal)), _ptr(seqlens_k), _stream_handle(dev))
+    _check(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                    scale: Optional[float] = None, causal: bool = False,
+                    out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Packed forward: q [Tq,Hq,d], k/v [Tk,Hkv,d], cu_seqlens int32 [S+1] on the GPU.
+
+    Returns O bf16 [Tq,Hq,d] and LSE fp32 [Hq,Tq].  Rows of a freshly allocated
+    O / LSE that belong to no sequence are left as zero.
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("expected q [Tq,Hq,d] and k, v [Tk,Hkv,d] of equal shape")
+    Tq, Hq, d = q.shape
+    _, Hkv, dk = k.shape
+    if dk != d:
+        raise ValueError("q and k disagree on head dim")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of equal length")
+    num_seqs = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.zeros_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None:
+        lse = torch.zeros((Hq, Tq), dtype=torch.float32, device=dev)
+    else:
+        _need(lse, "lse", torch.float32, dev)
+        if lse.shape != (Hq, Tq):
+            raise ValueError("lse must have shape [Hq,Tq]")
+    rc = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), num_seqs, Hq, Hkv, int(max_seqlen_q),
+                             int(max_seqlen_k), d, float(scale), int(bool(causal)),
+                             _stream_handle(dev))
+    _check(rc, "attn_fwd_varlen")
+    return out, lse

@@ -1,0 +1,124 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused exact-attention forward.
+ *
+ * The operation.  For every batch element b, query head h and query row i:
+ *
+ *     O[b,i,h,:] = sum_j P_ij V[b,j,h/G,:],   P_ij = exp(s_ij - LSE_i) for visible j,
+ *     s_ij       = scale * <Q[b,i,h,:], K[b,j,h/G,:]>,
+ *     LSE_i      = ln sum_{visible j} exp(s_ij)                     (natural log)
+ *
+ * i.e. O = softmax(scale * Q K^T) V taken row-wise over the visible keys, with
+ * the per-row log-sum-exp as a second output.  This is the problem statement of
+ * "FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for Asymmetric
+ * Hardware Scaling" (papercache summary), section 2.1, and of "059 ·
+ * FlashAttention" (wq-win), section 2; the log-sum-exp is the softmax
+ * normaliser the forward saves for the backward (FlashAttention notes
+ * (xwysyy), "Recomputation").  The N x N score and probability matrices are
+ * never written to memory: the kernel walks query blocks x key blocks with the
+ * online-softmax running maximum, running sum and unnormalised accumulator
+ * (FlashAttention V1 到 V4 (chengxuchu), section 3.4.1).
+ *
+ * Visibility.  Key j is visible to query i iff
+ *     (causal == 0 || j <= i)  &&  j < nk_b,
+ * where nk_b = Nk, or seqlens_k[b] clamped to [0, Nk] when seqlens_k is given.
+ * The causal mask is top-left aligned (query i sees keys 0..i) also when
+ * Nq != Nk.  A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Grouped-query heads: query head h reads key/value head h / G, G = Hq / Hkv.
+ *
+ * Types and layouts (all row-major, innermost dimension contiguous, no gaps):
+ *     q, o : bf16 [B, Nq, Hq, d]        k, v : bf16 [B, Nk, Hkv, d]
+ *     lse  : fp32 [B, Hq, Nq]
+ *   packed (varlen) form:
+ *     q, o : bf16 [Tq, Hq, d]           k, v : bf16 [Tk, Hkv, d]
+ *     lse  : fp32 [Hq, Tq],             Tq = cu_seqlens_q[num_seqs]
+ * d must be 64 or 128.  q, k, v and o must be 16-byte aligned; lse 4-byte.
+ * O is rounded to bf16 (round-to-nearest-even); LSE stays fp32.
+ *
+ * Memory and ownership.  Every pointer (q, k, v, o, lse, seqlens_k,
+ * cu_seqlens_*) is a DEVICE pointer owned by the caller.  The library
+ * allocates nothing, keeps no state besides a thread-local copy of the last
+ * HIP error, and is re-entrant.  o and lse must not overlap the inputs or each
+ * other.  All calls are asynchronous on `stream` (a hipStream_t; NULL means
+ * the default stream): they return after the launch and never synchronise.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; a
+ * non-zero return code means nothing was launched (except ATTN_ERR_LAUNCH,
+ * whose HIP code is kept for attn_last_hip_error()).  Device-resident values
+ * (seqlens_k, cu_seqlens_*) are not read on the host: seqlens_k entries are
+ * clamped to [0, Nk] in the kernel; cu_seqlens_* must be non-decreasing,
+ * start at 0 and stay within the packed buffers, and every sequence length
+ * must be at most the max_seqlen passed with it (rows past max_seqlen_q are
+ * not computed; keys past max_seqlen_k are not read).
+ */
+#ifndef EXACT_ATTENTION_18_AMD_ATTN_H
+#define EXACT_ATTENTION_18_AMD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  ATTN_ERR_HEAD_DIM = -2,  /* d is not 64 or 128                                  */
+  ATTN_ERR_HEADS = -3,     /* Hkv < 1, Hq < 1 or Hq % Hkv != 0                     */
+  ATTN_ERR_SIZE = -4,      /* negative size, or scale not finite and > 0          */
+  ATTN_ERR_LAUNCH = -5,    /* the HIP launch failed (see attn_last_hip_error)     */
+  ATTN_ERR_ALIGN = -6,     /* q, k, v or o not 16-byte aligned, lse not 4-byte    */
+  ATTN_ERR_TOO_LARGE = -7  /* grid or index range exceeds what the kernel handles */
+};
+
+/*
+ * Batched (padded) forward.
+ *   q, k, v   : device bf16 inputs, layouts above.
+ *   o, lse    : device outputs, written in full (every row of every head).
+ *   B, Nq, Nk : batch size, query and key sequence lengths (>= 0).  B == 0 or
+ *               Nq == 0 is a no-op returning ATTN_OK.  Nk == 0 gives O = 0,
+ *               LSE = -inf.
+ *   Hq, Hkv   : query and key/value head counts (Hq % Hkv == 0).
+ *   d         : head dimension, 64 or 128.
+ *   scale     : finite, > 0 (the workloads use 1/sqrt(d)).
+ *   causal    : non-zero for the causal mask.
+ *   seqlens_k : NULL, or device int32 [B] of valid key counts per batch
+ *               element (key padding); shared by all heads.
+ *   stream    : hipStream_t to launch on (NULL: default stream).
+ * Returns an attn_status.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
+             void* stream);
+
+/*
+ * Packed variable-length forward: num_seqs sequences stored back to back.
+ * Sequence z owns query rows cu_seqlens_q[z] .. cu_seqlens_q[z+1]-1 and keys
+ * cu_seqlens_k[z] .. cu_seqlens_k[z+1]-1; indices are local to the sequence
+ * for the causal rule.  cu_seqlens_q / cu_seqlens_k are device int32
+ * [num_seqs + 1].  max_seqlen_q / max_seqlen_k bound every sequence's length.
+ * Query rows that belong to no sequence are not written.  The packed layout
+ * is the batched one with the batch and sequence dimensions flattened
+ * (FlashAttention notes (xwysyy), code-structure overview, the "unpadded"
+ * interface; FlashAttention-4 (papercache summary), section 3.3, varlen
+ * metadata held on the device).
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
+                    int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                    int causal, void* stream);
+
+/* Static text for an attn_status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* hipError_t of the last failed launch on this thread (0 if none). */
+int attn_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_18_AMD_ATTN_H */
