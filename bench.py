@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run plain device-to-device copies of BYTES bytes (to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters of the forward to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the forward "
@@ -116,6 +119,15 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "copies": args.steps}), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     x = inputs.workload_inputs(w)

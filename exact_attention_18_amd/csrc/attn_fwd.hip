@@ -23,17 +23,27 @@
 //   max and row sum are therefore in-lane reductions plus one exchange with
 //   lane l^32, and the row statistics are per-lane scalars.
 // * The output is accumulated transposed too, O^T += V^T P^T, with the same
-//   instruction: A = a 32(d) x 16(key) slice of V^T from LDS, B = P^T taken
-//   straight from the score accumulators after conversion to bf16, so P
-//   never leaves registers.  For this the 16 keys an instruction consumes must
-//   sit in the same (lane-half, slot) positions in both operands; the score
-//   layout gives lane-half g the keys {4g..4g+3, 8+4g..8+4g+3} of each
-//   16-key group, so V^T is stored in LDS with the middle two 4-key chunks of
-//   every 16-key group swapped, which makes each A read one 16-byte load.
-// * K (row-major, padded rows) and V^T (padded rows) tiles are double-buffered
-//   in LDS; the next tile's global loads are issued into registers before the
-//   current tile's MFMAs and written to the other buffer after them, so each
-//   key step needs a single barrier.
+//   instruction: A = a 32(d) x 16(key) slice of V^T, B = P^T taken straight
+//   from the score accumulators after conversion to bf16, so P never leaves
+//   registers.  The 16 keys an instruction consumes must sit in the same
+//   (lane-half, slot) positions in both operands; the score layout gives
+//   lane-half g the keys {4g..4g+3, 8+4g..8+4g+3} of each 16-key group.  V
+//   stays row-major in LDS and each A operand is assembled from two gfx950
+//   transpose reads (ds_read_b64_tr_b16): in every 16-lane block, lane j
+//   addresses 4 consecutive d of key row j/4 and lane i receives the 4 keys of
+//   column i, which is exactly "4 consecutive keys of one d" per lane.
+// * K and V tiles (row-major, padded rows) are double-buffered in LDS; the
+//   next tile's global loads are issued into registers before the current
+//   tile's MFMAs and written to the other buffer after them, so each key step
+//   needs a single barrier.  Rows past the last needed key are loaded from a
+//   clamped (valid) row and masked, so the loads need no predication.
+// * Conditional rescaling (FlashAttention-4 (papercache summary), section
+//   3.1.4): the running max of a row is raised, and O and l rescaled, only
+//   when the new block's max exceeds it by more than tau = 8 (log2 units, a
+//   factor of 256); otherwise the block is accumulated against the stale max
+//   (probabilities up to 2^8 before normalisation).  The decision is made per
+//   wavefront -- if any lane needs it, the whole wave rescales -- so the skip
+//   is a uniform branch.  The final O / l and LSE = m + log2 l stay exact.
 // * Softmax runs in the exp2 domain with scale*log2(e) folded into one FMA per
 //   score; LSE is converted back to natural log in the epilogue.
 // * Causal: key blocks past the query block's last row are never visited, and
@@ -61,7 +71,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -77,15 +88,16 @@ struct Tile {
   static constexpr int DT = D / 32;                // 32-wide d blocks of O^T
   static constexpr int KS = D / 16;                // 16-deep d slices of S^T
   static constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
-  static constexpr int VSTR = BC + 8;              // LDS row stride of V^T (elements)
+  static constexpr int VSTR = D + 16;              // LDS row stride of V (elements)
   static constexpr int K_ELEMS = BC * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;      // one K + V^T buffer
-  static constexpr int K_CHUNKS = BC * D / 8 / kThreads;          // 16 B each
-  static constexpr int V_CHUNKS = (BC / 4) * (D / 8) / kThreads;  // 4 keys x 8 d each
-  static_assert(K_CHUNKS * kThreads * 8 == BC * D, "K tile split");
-  static_assert(V_CHUNKS * kThreads * 32 == BC * D, "V tile split");
+  static constexpr int V_ELEMS = BC * VSTR;
+  static constexpr int BUF = K_ELEMS + V_ELEMS;  // one K + V buffer
+  static constexpr int CHUNKS = BC * D / 8 / kThreads;  // 16-byte chunks per thread per tile
+  static_assert(CHUNKS * kThreads * 8 == BC * D, "tile split");
 };
+
+constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 
 struct Params {
   const __bf16* q;
@@ -107,12 +119,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position of the 4-key chunk `kc` (keys 4kc..4kc+3) in an LDS row of V^T:
-// within each 16-key group the chunks are stored in the order 0, 2, 1, 3.
-__device__ __forceinline__ int vt_pos(int kc) {
-  const int ci = kc & 3;
-  const int pc = (ci == 1) ? 2 : (ci == 2) ? 1 : ci;
-  return (kc >> 2) * 16 + pc * 4;
+// max(a, b, c) in one instruction.  fmaxf would make the compiler quiet
+// possible signalling NaNs of the MFMA results first (an extra instruction per
+// operand); scores here are finite or -inf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Two transpose reads of LDS, concatenated into one 8-element bf16 operand.
+__device__ __forceinline__ bf16x8 read_tr_pair(const __bf16* p0, const __bf16* p1) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -188,62 +210,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   if (CAUSAL) kv_end = min(nk, min(q0 + kBr, q_len));
   const int n_tiles = (kv_end + T::BC - 1) / T::BC;
 
-  // ---- tile staging: global -> registers -> LDS
-  u32x4 kr[T::K_CHUNKS];
-  u32x4 vr[T::V_CHUNKS][4];
+  // ---- tile staging: global -> registers -> LDS (K and V alike, 16-byte chunks)
+  // Buffer loads through a per-tile resource whose range ends at row kv_end:
+  // rows past it read as zero (and are masked below), so the loads need no
+  // predication and no per-lane 64-bit address arithmetic.
+  const uint32_t row_bytes = static_cast<uint32_t>(kv_stride) * 2u;
+  u32x4 kr[T::CHUNKS];
+  u32x4 vr[T::CHUNKS];
   auto load_tile = [&](int kv0) {
+    const int nrows = min(kv_end - kv0, T::BC);
+    const int nbytes = nrows * static_cast<int>(row_bytes);
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(kbase + kv0 * kv_stride), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(vbase + kv0 * kv_stride), (short)0, nbytes, kBufferFlags);
 #pragma unroll
-    for (int c = 0; c < T::K_CHUNKS; ++c) {
+    for (int c = 0; c < T::CHUNKS; ++c) {
       const int idx = tid + c * kThreads;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      const int key = kv0 + row;
-      kr[c] = key < kv_end ? *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + col)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int c = 0; c < T::V_CHUNKS; ++c) {
-      const int idx = tid + c * kThreads;
-      const int kc = idx % (T::BC / 4);
-      const int dc = idx / (T::BC / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + 4 * kc + r;
-        vr[c][r] = key < kv_end
-                       ? *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + dc * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
-      }
+      const uint32_t off = (idx / (D / 8)) * row_bytes + (idx % (D / 8)) * 16u;
+      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0);
+      vr[c] = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
     }
   };
   auto store_tile = [&](__bf16* buf) {
-    __bf16* ks = buf;
-    __bf16* vt = buf + T::K_ELEMS;
 #pragma unroll
-    for (int c = 0; c < T::K_CHUNKS; ++c) {
+    for (int c = 0; c < T::CHUNKS; ++c) {
       const int idx = tid + c * kThreads;
       const int row = idx / (D / 8);
       const int col = (idx % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(ks + row * T::KSTR + col) = kr[c];
-    }
-#pragma unroll
-    for (int c = 0; c < T::V_CHUNKS; ++c) {
-      const int idx = tid + c * kThreads;
-      const int kc = idx % (T::BC / 4);
-      const int dc = idx / (T::BC / 4);
-      const int pos = vt_pos(kc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t a0 = (vr[c][0][w] >> sh) & 0xffffu;
-        const uint32_t a1 = (vr[c][1][w] >> sh) & 0xffffu;
-        const uint32_t a2 = (vr[c][2][w] >> sh) & 0xffffu;
-        const uint32_t a3 = (vr[c][3][w] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2*>(vt + (dc * 8 + e) * T::VSTR + pos) =
-            u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
-      }
+      *reinterpret_cast<u32x4*>(buf + row * T::KSTR + col) = kr[c];
+      *reinterpret_cast<u32x4*>(buf + T::K_ELEMS + row * T::VSTR + col) = vr[c];
     }
   };
+
+  // Per-lane offset of the V transpose reads: key row 4g + (l%16)/4 of each
+  // 16-key group, d columns 16*((l/16)%2) + 4*(l%4) of each 32-wide d block.
+  const int v_lane = (4 * g + (l32 & 15) / 4) * T::VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 acc[T::DT];
 #pragma unroll
@@ -292,43 +294,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
             if (!vis) s[kt][r] = -INFINITY;
           }
       }
-      // Row max: in-lane, then with the partner lane holding the other keys.
-      float mx = -INFINITY;
+      // Row max: in-lane (two independent chains), then with the partner lane.
+      float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+        for (int r = 0; r < 16; r += 4) {
+          mx0 = max3f(mx0, s[kt][r], s[kt][r + 1]);
+          mx1 = max3f(mx1, s[kt][r + 2], s[kt][r + 3]);
+        }
+      float mx = max3f(mx0, mx1, -INFINITY);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      // Conditional rescale, decided for the whole wave.
+      const bool grow = mx > m_run + kTau;  // false while both are -inf
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) acc[dt] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
       // P = exp2(s*c - m), its row sum, and P^T as the bf16 B operand.
-      float lsum = 0.f;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
       bf16x8 pb[T::KT][2];
 #pragma unroll
       for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -m_use));
-          lsum += e;
+          ls[r & 3] += e;
           pb[kt][r >> 3][r & 7] = (__bf16)e;
         }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) acc[dt] *= alpha;
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-      // O^T += V^T P^T.
-      const __bf16* vt = cur + T::K_ELEMS;
+      // O^T += V^T P^T; V^T operands come from transpose reads of row-major V.
+      const __bf16* vl = cur + T::K_ELEMS + v_lane;
 #pragma unroll
       for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                vt + (dt * 32 + l32) * T::VSTR + kt * 32 + 16 * hh + 8 * g);
+            const __bf16* p0 = vl + (kt * 32 + 16 * hh) * T::VSTR + dt * 32;
+            const bf16x8 a = read_tr_pair(p0, p0 + 8 * T::VSTR);
             acc[dt] = mfma32(a, pb[kt][hh], acc[dt]);
           }
     }
