@@ -32,7 +32,14 @@
 //   transpose reads (ds_read_b64_tr_b16): in every 16-lane block, lane j
 //   addresses 4 consecutive d of key row j/4 and lane i receives the 4 keys of
 //   column i, which is exactly "4 consecutive keys of one d" per lane.
-// * K and V tiles (row-major, padded rows) are double-buffered in LDS; the
+// * V sits in LDS as "quad sub-tiles": for every group of 4 keys and every
+//   16 columns of d, the 4 x 16 block is stored as 128 contiguous bytes
+//   (groups in key order, blocks in d order).  A transpose read by 32 lanes
+//   then covers 256 contiguous bytes (no bank conflicts), and the 64 16-byte
+//   stores of a wave cover 1 KB contiguous bytes (none either).  K keeps
+//   row-major rows padded by 16 bytes, which spreads the 32 rows that a score
+//   operand read touches over distinct banks.
+// * K and V tiles are double-buffered in LDS; the
 //   next tile's global loads are issued into registers before the current
 //   tile's MFMAs and written to the other buffer after them, so each key step
 //   needs a single barrier.  Rows past the last needed key are loaded from a
@@ -62,6 +69,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -83,21 +91,23 @@ constexpr float kLn2 = 0.693147180559945309f;
 
 template <int D>
 struct Tile {
-  static constexpr int BC = (D == 64) ? 128 : 64;  // keys per step
+  static constexpr int BC = 64;                    // keys per step
   static constexpr int KT = BC / 32;               // 32-key MFMA blocks per step
   static constexpr int DT = D / 32;                // 32-wide d blocks of O^T
   static constexpr int KS = D / 16;                // 16-deep d slices of S^T
-  static constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
-  static constexpr int VSTR = D + 16;              // LDS row stride of V (elements)
-  static constexpr int K_ELEMS = BC * KSTR;
-  static constexpr int V_ELEMS = BC * VSTR;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;  // one K + V buffer
+  static constexpr int QUAD = 4 * D;               // V elements per 4-key group in LDS
+  static constexpr int K_ELEMS = BC * D;           // one K tile
+  static constexpr int V_ELEMS = BC * D;           // one V tile
   static constexpr int CHUNKS = BC * D / 8 / kThreads;  // 16-byte chunks per thread per tile
   static_assert(CHUNKS * kThreads * 8 == BC * D, "tile split");
 };
 
 constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
-constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
+constexpr int kBufferFlags = 0x00020000;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;  // buffer resource word 3 for raw 32-bit access (gfx9)
 
 struct Params {
   const __bf16* q;
@@ -128,6 +138,21 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// Reductions over the lane pair (l, l^32).  v_permlane32_swap exchanges the
+// upper half-wave of one register with the lower half-wave of another; with
+// x in both, every lane ends up holding x_l in one result and x_(l^32) in the
+// other, so a symmetric combine of the two needs no lane select.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), -INFINITY);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Two transpose reads of LDS, concatenated into one 8-element bf16 operand.
 __device__ __forceinline__ bf16x8 read_tr_pair(const __bf16* p0, const __bf16* p1) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -140,11 +165,17 @@ __device__ __forceinline__ bf16x8 read_tr_pair(const __bf16* p0, const __bf16* p
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::BUF];
+  // Four LDS tiles, as distinct arrays: with the tile parity known at compile
+  // time the compiler can tell a DMA write to one tile from a read of another
+  // and does not make the read wait for the DMA.
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[T::K_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[T::K_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[T::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[T::V_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -194,162 +225,285 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   const __bf16* vbase = p.v + k_row0 * kv_stride + (long)hkv * D;
 
   // ---- this lane's query row, held as the B operand of S^T = K Q^T
-  const int qrow = q0 + wave * kRowsPerWave + l32;
+  const int wrow0 = q0 + wave * kRowsPerWave;
+  const int wrow_last = wrow0 + kRowsPerWave - 1;
+  const int qrow = wrow0 + l32;
   bf16x8 qf[T::KS];
-  if (qrow < q_len) {
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + qrow * q_stride + ks * 16 + 8 * g);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) qf[ks] = bf16x8{};
-  }
+  for (int ks = 0; ks < T::KS; ++ks)
+    qf[ks] = qrow < q_len
+                 ? *reinterpret_cast<const bf16x8*>(qbase + qrow * q_stride + ks * 16 + 8 * g)
+                 : bf16x8{};
 
   // Keys this workgroup needs: all visible keys of its rows.
   int kv_end = nk;
   if (CAUSAL) kv_end = min(nk, min(q0 + kBr, q_len));
   const int n_tiles = (kv_end + T::BC - 1) / T::BC;
 
-  // ---- tile staging: global -> registers -> LDS (K and V alike, 16-byte chunks)
-  // Buffer loads through a per-tile resource whose range ends at row kv_end:
-  // rows past it read as zero (and are masked below), so the loads need no
-  // predication and no per-lane 64-bit address arithmetic.
+  // ---- global -> LDS tile loads (buffer_load ... lds, 16 bytes per lane).
+  // Instruction i of wave w fills the 1 KB of LDS slots [(i*kWaves + w)*64, +64)
+  // of the tile, one 16-byte slot per lane; each lane fetches the global
+  // chunk that belongs in its slot under the tile's LDS layout:
+  //   K, 16-row groups: slot c holds row 16*(c / (16*D/8)) + c%16, 16-byte
+  //     column (c % (16*D/8)) / 16;
+  //   V, quad sub-tiles: slot c holds key 4*(c / (D/2)) + (c%8)/2, columns
+  //     16*((c % (D/2)) / 8) + 8*(c%2) .. +7.
   const uint32_t row_bytes = static_cast<uint32_t>(kv_stride) * 2u;
-  u32x4 kr[T::CHUNKS];
-  u32x4 vr[T::CHUNKS];
-  auto load_tile = [&](int kv0) {
+  auto k_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
+    const int rem16 = c % (16 * (D / 8));
+    *row = 16 * (c / (16 * (D / 8))) + rem16 % 16;
+    *colb = (rem16 / 16) * 16;
+  };
+  auto v_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
+    const int w = c % (D / 2);
+    *row = 4 * (c / (D / 2)) + (w % 8) / 2;
+    *colb = (16 * (w / 8) + 8 * (w % 2)) * 2;
+  };
+  uint32_t kgoff[T::CHUNKS], vgoff[T::CHUNKS];  // byte offsets within a full tile
+#pragma unroll
+  for (int i = 0; i < T::CHUNKS; ++i) {
+    const int c = (i * kWaves + wave) * 64 + lane;
+    int row, colb;
+    k_slot(c, &row, &colb);
+    kgoff[i] = row * row_bytes + colb;
+    v_slot(c, &row, &colb);
+    vgoff[i] = row * row_bytes + colb;
+  }
+  // Rows at or past kv_end (only in the last tile) are fetched from row
+  // kv_end - 1 (valid memory) and masked out of the scores, so no lane ever
+  // multiplies uninitialised LDS.
+  auto issue_tile = [&](const __bf16* base, __bf16* dst, const uint32_t* goff, bool is_v,
+                        int kv0) __attribute__((always_inline)) {
     const int nrows = min(kv_end - kv0, T::BC);
-    const int nbytes = nrows * static_cast<int>(row_bytes);
-    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(kbase + kv0 * kv_stride), (short)0, nbytes, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(vbase + kv0 * kv_stride), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(base + kv0 * kv_stride), (short)0, nrows * (int)row_bytes,
+        kBufferFlags);
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c) {
-      const int idx = tid + c * kThreads;
-      const uint32_t off = (idx / (D / 8)) * row_bytes + (idx % (D / 8)) * 16u;
-      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0);
-      vr[c] = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
-    }
-  };
-  auto store_tile = [&](__bf16* buf) {
-#pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c) {
-      const int idx = tid + c * kThreads;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(buf + row * T::KSTR + col) = kr[c];
-      *reinterpret_cast<u32x4*>(buf + T::K_ELEMS + row * T::VSTR + col) = vr[c];
+    for (int i = 0; i < T::CHUNKS; ++i) {
+      uint32_t off = goff[i];
+      if (nrows < T::BC) {
+        int row, colb;
+        const int c = (i * kWaves + wave) * 64 + lane;
+        if (is_v) v_slot(c, &row, &colb); else k_slot(c, &row, &colb);
+        off = (uint32_t)min(row, nrows - 1) * row_bytes + (uint32_t)colb;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          res, (__attribute__((address_space(3))) void*)(dst + (i * kWaves + wave) * 512), 16,
+          off, 0, 0, 0);
     }
   };
 
-  // Per-lane offset of the V transpose reads: key row 4g + (l%16)/4 of each
-  // 16-key group, d columns 16*((l/16)%2) + 4*(l%4) of each 32-wide d block.
-  const int v_lane = (4 * g + (l32 & 15) / 4) * T::VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // ---- per-lane LDS read offsets (elements)
+  // K (A operand of S^T): row kt*32 + l32, 16-byte column 2ks + g.
+  const int k_lane = ((l32 >> 4) * (D / 8) + g) * 128 + (l32 & 15) * 8;
+  // V (transpose reads): key group g of each 8-key half, 16-column block
+  // (l/16)%2 of each 32-wide d block, row (l%16)/4, columns 4*(l%4)..+3.
+  const int v_lane = g * T::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
 
+  const float c = p.c;
+  // A wave skips key tiles lying wholly above its rows (causal).
+  auto active = [&](int tile) __attribute__((always_inline)) { return !CAUSAL || tile * T::BC <= wrow_last; };
+  auto needs_mask = [&](int tile) __attribute__((always_inline)) {
+    const int kv0 = tile * T::BC;
+    return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0);
+  };
+
+  // ---- per-lane state: S^T of one tile (32 keys x 2 blocks of this lane's
+  // row), P^T of one tile as bf16 MFMA operands, O^T, row statistics.
+  f32x16 sv[T::KT];
+  bf16x8 pv_op[T::KT][2];
   f32x16 acc[T::DT];
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY;  // running max, log2 domain (scores times scale*log2 e)
   float l_run = 0.f;        // this lane's half of the running sum
-  const float c = p.c;
-  const int wrow0 = q0 + wave * kRowsPerWave;
-  const int wrow_last = wrow0 + kRowsPerWave - 1;
+  float alpha = 1.f;
+  bool rescale_o = false;   // wave-uniform: O must be multiplied by alpha
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(smem);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kv0 = j * T::BC;
-    const __bf16* cur = smem + (j & 1) * T::BUF;
-    __bf16* nxt = smem + ((j + 1) & 1) * T::BUF;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(kv0 + T::BC);
-
-    if (!CAUSAL || kv0 <= wrow_last) {  // uniform over the wave
-      // S^T block kt: keys kv0+32kt.., queries of this wave.
-      f32x16 s[T::KT];
-#pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt) {
-        s[kt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + (kt * 32 + l32) * T::KSTR +
-                                                             ks * 16 + 8 * g);
-          s[kt] = mfma32(a, qf[ks], s[kt]);
-        }
-      }
-      // Masks, only on blocks crossing the key tail or the diagonal.
-      const bool need_mask = (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0);
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = key < nk && (!CAUSAL || key <= qrow);
-            if (!vis) s[kt][r] = -INFINITY;
-          }
-      }
-      // Row max: in-lane (two independent chains), then with the partner lane.
-      float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          mx0 = max3f(mx0, s[kt][r], s[kt][r + 1]);
-          mx1 = max3f(mx1, s[kt][r + 2], s[kt][r + 3]);
-        }
-      float mx = max3f(mx0, mx1, -INFINITY);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-      // Conditional rescale, decided for the whole wave.
-      const bool grow = mx > m_run + kTau;  // false while both are -inf
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) acc[dt] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // P = exp2(s*c - m), its row sum, and P^T as the bf16 B operand.
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-      bf16x8 pb[T::KT][2];
-#pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -m_use));
-          ls[r & 3] += e;
-          pb[kt][r >> 3][r & 7] = (__bf16)e;
-        }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-      // O^T += V^T P^T; V^T operands come from transpose reads of row-major V.
-      const __bf16* vl = cur + T::K_ELEMS + v_lane;
-#pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) {
-            const __bf16* p0 = vl + (kt * 32 + 16 * hh) * T::VSTR + dt * 32;
-            const bf16x8 a = read_tr_pair(p0, p0 + 8 * T::VSTR);
-            acc[dt] = mfma32(a, pb[kt][hh], acc[dt]);
-          }
+  // ---- slice plan of one iteration (tile j; one MFMA per slice).  Slices
+  // 0..kPv-1 are the P V MFMAs of tile j-1, slices kPv.. the score MFMAs of
+  // tile j+1 (key block 0, then 1).  The softmax of tile j rides along:
+  //   P V of key block 0   | row max of S_j
+  //   P V of key block 1   | rescale decision; exponentials of S_j block 0 -> P block 0
+  //   scores, key block 0  | exponentials of S_j block 1 -> P block 1
+  //   scores, key block 1  |
+  // so every read of S_j / P_{j-1} precedes, in program order, the write of
+  // S_{j+1} / P_j to the same registers, and no second copy is kept.  Slices
+  // are separated by scheduling barriers (source order is the schedule) and
+  // each one reads the LDS operand of the next ahead of use.
+  constexpr int kPv = T::KT * 2 * T::DT;  // P V slices (one V operand each)
+  constexpr int kS = T::KT * T::KS;       // score slices (one K operand each)
+  constexpr int kSlices = kPv + kS;
+  constexpr int kDecide = kPv / 2;        // first slice of P V key block 1
+  constexpr int kAhead = 2;               // LDS read lookahead, in slices
+  static_assert(T::KT == 2 && kDecide >= 2 && 32 % kDecide == 0, "slice plan");
+  auto load_operand = [&](int sl, const __bf16* vb, const __bf16* kb) __attribute__((always_inline)) -> bf16x8 {
+    if (sl < kPv) {
+      const int kt = sl / (2 * T::DT), hh = (sl / T::DT) % 2, dt = sl % T::DT;
+      const __bf16* p0 = vb + v_lane + (8 * kt + 4 * hh) * T::QUAD + dt * 128;
+      return read_tr_pair(p0, p0 + 2 * T::QUAD);
     }
+    const int kt = (sl - kPv) / T::KS, ks = (sl - kPv) % T::KS;
+    return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (D / 8) + 2 * ks) * 128);
+  };
+  // Exponentials of S_j key block kt, score registers [r0, r1).
+  auto exps = [&](int kt, int r0, int r1, float* ls, const float m_use) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = r0; r < r1; r += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], c, -m_use));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
+      ls[0] += e0;
+      ls[1] += e1;
+      pv_op[kt][r >> 3][r & 7] = (__bf16)e0;
+      pv_op[kt][r >> 3][(r & 7) + 1] = (__bf16)e1;
+    }
+  };
+  auto apply_mask = [&](int tile) __attribute__((always_inline)) {
+    const int kv0 = tile * T::BC;
+#pragma unroll
+    for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool vis = key < nk && (!CAUSAL || key <= qrow);
+        if (!vis) sv[kt][r] = -INFINITY;
+      }
+  };
+  // One iteration.  vb: LDS tile of V_{j-1}; kb: LDS tile of K_{j+1}.  FAST
+  // (compile-time) is the steady state: a predecessor and an active successor
+  // exist and tile j needs no mask, so every predicate folds to true.
+  auto iteration = [&](int j, const __bf16* vb, const __bf16* kb, auto fast_tag) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const bool do_pv = FAST || (j >= 1 && active(j - 1));
+    const bool do_sm = FAST || active(j);
+    const bool do_s = FAST || (j + 1 < n_tiles && active(j + 1));
+    if (!FAST && do_sm && needs_mask(j)) apply_mask(j);
+    float m0 = -INFINITY, m1 = -INFINITY, m_use = 0.f;
+    float ls[2] = {0.f, 0.f};
+    // LDS operands are read kAhead slices before their MFMA.
+    bf16x8 opnd[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      opnd[i] = bf16x8{};
+      if (i < kPv ? do_pv : do_s) opnd[i] = load_operand(i, vb, kb);
+    }
+#pragma unroll
+    for (int sl = 0; sl < kSlices; ++sl) {
+      const bf16x8 a = opnd[sl % kAhead];
+      const int nx = sl + kAhead;
+      if (nx < kSlices && (nx < kPv ? do_pv : do_s)) opnd[sl % kAhead] = load_operand(nx, vb, kb);
+      if (sl < kPv) {
+        const int kt = sl / (2 * T::DT), hh = (sl / T::DT) % 2, dt = sl % T::DT;
+        if (do_pv) acc[dt] = mfma32(a, pv_op[kt][hh], acc[dt]);
+      } else {
+        const int kt = (sl - kPv) / T::KS, ks = (sl - kPv) % T::KS;
+        if (do_s) sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
+      }
+      if (do_sm) {
+        if (sl < kDecide) {
+          // row max over the 32 scores of this lane, spread over kDecide slices
+          constexpr int per = 32 / kDecide;
+          const int e0 = sl * per;
+#pragma unroll
+          for (int e = e0; e < e0 + per; e += 4) {
+            m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
+            m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
+          }
+        } else if (sl == kDecide) {
+          // Conditional rescale (tau), decided for the whole wave.
+          const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
+          const bool any = __builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0;
+          const float m_new = any ? fmaxf(m_run, mx) : m_run;
+          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+          m_use = (m_new == -INFINITY) ? 0.f : m_new;
+          rescale_o = rescale_o || any;
+        } else if (sl < kPv) {
+          // exponentials of key block 0 over slices kDecide+1 .. kPv-1
+          constexpr int nsl = kPv - kDecide - 1;
+          const int i = sl - kDecide - 1;
+          exps(0, 2 * ((i * 8) / nsl), 2 * (((i + 1) * 8) / nsl), ls, m_use);
+        } else if (sl < kPv + T::KS) {
+          // exponentials of key block 1 over the score slices of key block 0
+          const int i = sl - kPv;
+          exps(1, 2 * ((i * 8) / T::KS), 2 * (((i + 1) * 8) / T::KS), ls, m_use);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (do_sm) l_run += ls[0] + ls[1];
+    // The deferred O rescale: after the P V of tile j-1 (relative to the old
+    // max), before the P V of tile j.
+    if (rescale_o) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) acc[dt] *= alpha;
+      rescale_o = false;
+    }
+  };
+  // P V of the last tile (its V was loaded during the last iteration).
+  auto last_pv = [&](const __bf16* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sl = 0; sl < kPv; ++sl) {
+      const int kt = sl / (2 * T::DT), hh = (sl / T::DT) % 2, dt = sl % T::DT;
+      acc[dt] = mfma32(load_operand(sl, vb, vb), pv_op[kt][hh], acc[dt]);
+    }
+  };
 
-    if (has_next) store_tile(nxt);
-    __syncthreads();
+  // ---- prologue: K_0, K_1 in LDS, scores of tile 0
+  if (n_tiles > 0) issue_tile(kbase, k_lds0, kgoff, false, 0);
+  if (n_tiles > 1) issue_tile(kbase, k_lds1, kgoff, false, T::BC);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n_tiles > 0 && active(0)) {
+#pragma unroll
+    for (int sl = kPv; sl < kSlices; ++sl) {
+      const int kt = (sl - kPv) / T::KS, ks = (sl - kPv) % T::KS;
+      sv[kt] = mfma32(load_operand(sl, v_lds0, k_lds0), qf[ks], ks == 0 ? f32x16{} : sv[kt]);
+    }
   }
+  __syncthreads();  // every wave is done with K_0 before K_2 overwrites it
+
+  // ---- iterations.  Iteration j loads K_{j+2} into the tile K_j used and
+  // V_j into the tile V_{j-2} used, reads V_{j-1} and K_{j+1}.
+  auto step_static = [&](int j, auto par, auto fast_tag) __attribute__((always_inline)) {
+    constexpr bool P = decltype(par)::value;  // parity of j
+    __bf16* kw = P ? k_lds1 : k_lds0;
+    __bf16* vw = P ? v_lds1 : v_lds0;
+    const __bf16* kr = P ? k_lds0 : k_lds1;
+    const __bf16* vr = P ? v_lds0 : v_lds1;
+    if (j + 2 < n_tiles) issue_tile(kbase, kw, kgoff, false, (j + 2) * T::BC);
+    issue_tile(vbase, vw, vgoff, true, j * T::BC);
+    iteration(j, vr, kr, fast_tag);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  auto step_dynamic = [&](int j) __attribute__((always_inline)) {  // buffers chosen at run time (generic iterations)
+    const bool P = j & 1;
+    if (j + 2 < n_tiles) issue_tile(kbase, P ? k_lds1 : k_lds0, kgoff, false, (j + 2) * T::BC);
+    issue_tile(vbase, P ? v_lds1 : v_lds0, vgoff, true, j * T::BC);
+    iteration(j, P ? v_lds0 : v_lds1, P ? k_lds0 : k_lds1, std::false_type{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // Steady-state iterations form one contiguous range [1, j_hi) per wave;
+  // it runs unrolled by two so that the tile parity (hence every LDS buffer)
+  // is a compile-time choice.  Every iteration has exactly one barrier, so
+  // all waves agree on the barrier count.
+  int j_hi = 1;
+  while (j_hi + 1 < n_tiles && active(j_hi + 1) && !needs_mask(j_hi)) ++j_hi;
+  if (n_tiles > 0) step_dynamic(0);
+  int j = 1;
+  for (; j + 1 < j_hi; j += 2) {
+    step_static(j, std::true_type{}, std::true_type{});
+    step_static(j + 1, std::false_type{}, std::true_type{});
+  }
+  if (j < j_hi) step_static(j++, std::true_type{}, std::true_type{});
+  for (j = max(j, 1); j < n_tiles; ++j) step_dynamic(j);
+  if (n_tiles > 0 && active(n_tiles - 1)) last_pv(((n_tiles - 1) & 1) ? v_lds1 : v_lds0);
 
   // ---- epilogue: O = o / l in bf16, LSE = (m + log2 l) ln 2
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (qrow < q_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* orow = p.o + (q_row0 + qrow) * q_stride + (long)h * D;
