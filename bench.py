@@ -21,6 +21,7 @@ cpu_baseline: the CPU oracle as it stands, timed on this host on a bounded
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +35,29 @@ from exact_attention_18_amd import attn, inputs
 
 PEAK_BF16_TFLOPS = 2516.6
 METRIC = "attn fwd TFLOP/s bf16 hd128 causal N=8192 + % of MFMA bf16 peak"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_18_amd", "csrc", "attn_fwd.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 summary of this workload.
+
+    The summary records FETCH_SIZE / WRITE_SIZE of the forward scaled by a
+    plain-copy calibration, and the sha256 of the kernel source it was taken
+    on; a summary of another kernel version gives None.
+    """
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "-", "#", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def algorithmic_flops(w: inputs.Workload, x) -> float:
@@ -183,7 +207,7 @@ def main():
         "pct_of_mfma_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel_ms": round(kernel_ms, 5)},
+                     "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
