@@ -77,6 +77,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   // ---- per-lane state: S^T of one tile (32 keys x 2 blocks of this lane's
   // row), P^T of one tile as bf16 MFMA operands, O^T, row statistics.
   f32x16 sv[T::KT];
-  bf16x8 pv_op[T::KT][2];
+  u32x4 pv_op[T::KT][2];  // P^T operands, bf16 pairs packed in 32-bit words
   f32x16 acc[T::DT];
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) acc[dt] = f32x16{};
@@ -346,7 +347,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     const int kt = (sl - kPv) / T::KS, ks = (sl - kPv) % T::KS;
     return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (D / 8) + 2 * ks) * 128);
   };
-  // Exponentials of S_j key block kt, score registers [r0, r1).
+  // Exponentials of S_j key block kt, score registers [r0, r1).  The packed
+  // bf16 pair and the partial row sums are pinned with an empty asm so the
+  // compiler cannot sink this work out of its slice towards the next
+  // iteration's use.
   auto exps = [&](int kt, int r0, int r1, float* ls, const float m_use) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = r0; r < r1; r += 2) {
@@ -354,8 +358,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
       const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
       ls[0] += e0;
       ls[1] += e1;
-      pv_op[kt][r >> 3][r & 7] = (__bf16)e0;
-      pv_op[kt][r >> 3][(r & 7) + 1] = (__bf16)e1;
+      const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+      uint32_t u = __builtin_bit_cast(uint32_t, pk);
+      asm volatile("" : "+v"(u), "+v"(ls[0]), "+v"(ls[1]));
+      pv_op[kt][r >> 3][(r & 7) >> 1] = u;
     }
   };
   auto apply_mask = [&](int tile) __attribute__((always_inline)) {
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
       if (nx < kSlices && (nx < kPv ? do_pv : do_s)) opnd[sl % kAhead] = load_operand(nx, vb, kb);
       if (sl < kPv) {
         const int kt = sl / (2 * T::DT), hh = (sl / T::DT) % 2, dt = sl % T::DT;
-        if (do_pv) acc[dt] = mfma32(a, pv_op[kt][hh], acc[dt]);
+        if (do_pv) acc[dt] = mfma32(a, __builtin_bit_cast(bf16x8, pv_op[kt][hh]), acc[dt]);
       } else {
         const int kt = (sl - kPv) / T::KS, ks = (sl - kPv) % T::KS;
         if (do_s) sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int sl = 0; sl < kPv; ++sl) {
       const int kt = sl / (2 * T::DT), hh = (sl / T::DT) % 2, dt = sl % T::DT;
-      acc[dt] = mfma32(load_operand(sl, vb, vb), pv_op[kt][hh], acc[dt]);
+      acc[dt] = mfma32(load_operand(sl, vb, vb), __builtin_bit_cast(bf16x8, pv_op[kt][hh]), acc[dt]);
     }
   };
 
