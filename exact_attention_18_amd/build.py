@@ -11,6 +11,7 @@ harmless notice that it does not know this feature).
 
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -57,6 +58,12 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
+    # Every symbol must resolve (e.g. host stubs of all kernel instantiations).
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as exc:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {exc}") from exc
     os.replace(tmp, LIB)
     return LIB
 
