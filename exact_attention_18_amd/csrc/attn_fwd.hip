@@ -11,51 +11,44 @@
 // the end.  The work split (one workgroup per query block, inner loop over key
 // blocks) is the FlashAttention-2 partitioning (chengxuchu, section 4.3).
 //
-// CDNA4 mapping
-// -------------
-// * 4 waves (wave64) per workgroup; each wave owns 32 query rows, so a
-//   workgroup covers kBr = 128 query rows.
-// * Scores are computed transposed, S^T = K Q^T, with
-//   v_mfma_f32_32x32x16_bf16: A = a 32-key slice of K read from LDS, B = the
-//   wave's 32 query rows held in VGPRs for the whole kernel.  In the 32x32
-//   accumulator layout lane l holds column l%32 (one query row) and 16 of the
-//   32 key rows; lanes l and l^32 hold the other half of the same row.  Row
-//   max and row sum are therefore in-lane reductions plus one exchange with
-//   lane l^32, and the row statistics are per-lane scalars.
+// Shared CDNA4 mapping
+// --------------------
+// * Each wave (wave64) owns 32 query rows.  Scores are computed transposed,
+//   S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = a 32-key slice of K read
+//   from LDS, B = the wave's 32 query rows held in VGPRs for the whole
+//   kernel.  In the 32x32 accumulator layout lane l holds column l%32 (one
+//   query row) and 16 of the 32 key rows; lanes l and l^32 hold the other half
+//   of the same row.  Row max and row sum are therefore in-lane reductions
+//   plus one exchange with lane l^32 (v_permlane32_swap), and the row
+//   statistics are per-lane scalars.
 // * The output is accumulated transposed too, O^T += V^T P^T, with the same
 //   instruction: A = a 32(d) x 16(key) slice of V^T, B = P^T taken straight
 //   from the score accumulators after conversion to bf16, so P never leaves
 //   registers.  The 16 keys an instruction consumes must sit in the same
 //   (lane-half, slot) positions in both operands; the score layout gives
-//   lane-half g the keys {4g..4g+3, 8+4g..8+4g+3} of each 16-key group.  V
-//   stays row-major in LDS and each A operand is assembled from two gfx950
-//   transpose reads (ds_read_b64_tr_b16): in every 16-lane block, lane j
-//   addresses 4 consecutive d of key row j/4 and lane i receives the 4 keys of
-//   column i, which is exactly "4 consecutive keys of one d" per lane.
-// * V sits in LDS as "quad sub-tiles": for every group of 4 keys and every
-//   16 columns of d, the 4 x 16 block is stored as 128 contiguous bytes
-//   (groups in key order, blocks in d order).  A transpose read by 32 lanes
-//   then covers 256 contiguous bytes (no bank conflicts), and the 64 16-byte
-//   stores of a wave cover 1 KB contiguous bytes (none either).  K keeps
-//   row-major rows padded by 16 bytes, which spreads the 32 rows that a score
-//   operand read touches over distinct banks.
-// * K and V tiles are double-buffered in LDS; the
-//   next tile's global loads are issued into registers before the current
-//   tile's MFMAs and written to the other buffer after them, so each key step
-//   needs a single barrier.  Rows past the last needed key are loaded from a
-//   clamped (valid) row and masked, so the loads need no predication.
+//   lane-half g the keys {4g..4g+3, 8+4g..8+4g+3} of each 16-key group.  Each
+//   A operand of V^T is assembled from two gfx950 transpose reads
+//   (ds_read_b64_tr_b16): in every 16-lane block, lane j addresses 4
+//   consecutive d of key row j/4 and lane i receives the 4 keys of column i.
+// * LDS tile layouts (64 keys per tile).  K: 16-row groups, 16-byte chunk
+//   major -- element offset ((row/16)*(D/8) + chunk)*128 + (row%16)*8 -- so the
+//   32 lanes of a score-operand read touch 32 distinct 16-byte bank groups.
+//   V: "quad sub-tiles", each 4 keys x 16 d stored as 128 contiguous bytes
+//   (groups in key order, blocks in d order), so a transpose read by 32 lanes
+//   covers 256 contiguous bytes.  Both are conflict-free, and a tile is
+//   filled by 1 KB contiguous stores (one 16-byte chunk per lane).
+// * Rows past the last valid key are read as zeros (buffer-resource range
+//   check) or from a clamped valid row, and masked to -inf in the scores.
 // * Conditional rescaling (FlashAttention-4 (papercache summary), section
 //   3.1.4): the running max of a row is raised, and O and l rescaled, only
 //   when the new block's max exceeds it by more than tau = 8 (log2 units, a
-//   factor of 256); otherwise the block is accumulated against the stale max
-//   (probabilities up to 2^8 before normalisation).  The decision is made per
-//   wavefront -- if any lane needs it, the whole wave rescales -- so the skip
-//   is a uniform branch.  The final O / l and LSE = m + log2 l stay exact.
+//   factor of 256); otherwise the block is accumulated against the stale max.
+//   The decision is per wavefront (a ballot), so the skip is a uniform branch.
+//   The final O / l and LSE = m + log2 l stay exact.
 // * Softmax runs in the exp2 domain with scale*log2(e) folded into one FMA per
 //   score; LSE is converted back to natural log in the epilogue.
-// * Causal: key blocks past the query block's last row are never visited, and
-//   a wave skips a key block lying wholly above its rows; masks are applied
-//   only on blocks that cross the diagonal or the key tail.
+// * Causal: key blocks past the query block's last row are never visited;
+//   masks are applied only on blocks that cross the diagonal or the key tail.
 // * Grid order: workgroup ids are assigned round-robin to the 8 XCDs, so the
 //   id is first remapped to make each XCD's share a contiguous run of logical
 //   work items; logical order is batch, KV head, query block (longest first
@@ -63,6 +56,20 @@
 //   workgroups resident on one XCD read the same K/V from its L2
 //   (longest-processing-time-first scheduling and head grouping of
 //   FlashAttention-4 (papercache summary), section 3.3).
+//
+// Two kernels
+// -----------
+// * d = 128: attn_fwd_pp_kernel, 8 waves / 256 query rows per workgroup in
+//   two groups of four; the two waves sharing a SIMD belong to different
+//   groups and run half a period apart, so one feeds the matrix core (scores
+//   of tile j, then P V of tile j-1) while the other computes its softmax --
+//   the CDNA form of the ping-pong of FlashAttention-4 (papercache summary),
+//   section 3.1.2.  One workgroup barrier per half period.  K/V tiles move
+//   global -> VGPRs -> LDS (16-byte loads, one tile per group per period,
+//   double-buffered), the LDS stores spread over the MFMA phase.
+// * d = 64: attn_fwd_kernel, 4 waves / 128 query rows per workgroup, each
+//   wave interleaving its own softmax with its MFMAs slice by slice; K/V tiles
+//   move global -> LDS directly (buffer_load ... lds), K two tiles ahead.
 
 #include <hip/hip_runtime.h>
 
@@ -103,12 +110,11 @@ struct Tile {
   static_assert(CHUNKS * kThreads * 8 == BC * D, "tile split");
 };
 
+constexpr int kWaitVm0 = 0;  // s_waitcnt immediate: every counter zero
+// s_waitcnt lgkmcnt(0) only (gfx9 encoding: vmcnt 63, expcnt 7).
+constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
 constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
-constexpr int kBufferFlags = 0x00020000;
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;  // buffer resource word 3 for raw 32-bit access (gfx9)
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 
 struct Params {
   const __bf16* q;
@@ -152,6 +158,14 @@ __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // Two transpose reads of LDS, concatenated into one 8-element bf16 operand.
@@ -528,13 +542,350 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong forward: 8 waves per workgroup in two groups of 4.  The two waves
+// that share a SIMD belong to different groups.  Each wave alternates an MFMA
+// phase (scores of tile j, then P V of tile j-1) and a VALU phase (softmax of
+// tile j); group 1 runs half a period behind group 0, so while one wave of a
+// SIMD feeds the matrix core the other computes its exponentials.  One
+// workgroup barrier per half period keeps the groups in step.
+constexpr int kPpWaves = 8;
+constexpr int kPpThreads = 64 * kPpWaves;
+constexpr int kPpBr = kPpWaves * kRowsPerWave;  // 256 query rows per workgroup
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
+  using T = Tile<D>;
+  constexpr int CH = T::BC * D / 8 / (kPpThreads / 2);  // 16-byte chunks per thread per tile (one group moves a tile)
+  static_assert(CH >= 1 && CH * kPpThreads * 8 == 2 * T::BC * D, "tile split");
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[T::K_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[T::K_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[T::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[T::V_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int chunk = 2 * (wave & 3) + grp;  // 32-row chunk of the query block
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int n = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds;
+  const int per = n / kXcds;
+  const int rem = n % kXcds;
+  int t = xcd * per + min(xcd, rem) + bid / kXcds;
+  const int gi = t % p.G;
+  t /= p.G;
+  const int qbi = t % p.nqb;
+  t /= p.nqb;
+  const int hkv = t % p.Hkv;
+  const int b = t / p.Hkv;
+  const int qb = CAUSAL ? (p.nqb - 1 - qbi) : qbi;
+  const int h = hkv * p.G + gi;
+
+  int q_len, nk;
+  long q_row0, k_row0, lse_base, lse_hstride;
+  if (VARLEN) {
+    const int qs = p.cu_q[b], qe = p.cu_q[b + 1];
+    const int ks = p.cu_k[b], ke = p.cu_k[b + 1];
+    q_len = min(max(qe - qs, 0), p.Nq);
+    nk = min(max(ke - ks, 0), p.Nk);
+    q_row0 = qs;
+    k_row0 = ks;
+    lse_base = qs;
+    lse_hstride = p.cu_q[p.num_seqs];
+  } else {
+    q_len = p.Nq;
+    nk = p.Nk;
+    if (p.seqlens_k != nullptr) nk = min(max(p.seqlens_k[b], 0), p.Nk);
+    q_row0 = (long)b * p.Nq;
+    k_row0 = (long)b * p.Nk;
+    lse_base = (long)b * p.Hq * p.Nq;
+    lse_hstride = p.Nq;
+  }
+  const int q0 = qb * kPpBr;
+  if (q0 >= q_len) return;  // uniform over the workgroup, before any barrier
+
+  const long q_stride = (long)p.Hq * D;
+  const long kv_stride = (long)p.Hkv * D;
+  const __bf16* qbase = p.q + q_row0 * q_stride + (long)h * D;
+  const __bf16* kbase = p.k + k_row0 * kv_stride + (long)hkv * D;
+  const __bf16* vbase = p.v + k_row0 * kv_stride + (long)hkv * D;
+
+  const int wrow0 = q0 + chunk * kRowsPerWave;
+  const int qrow = wrow0 + l32;
+  bf16x8 qf[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks)
+    qf[ks] = qrow < q_len
+                 ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
+                 : bf16x8{};
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // qf ready before any tile load is in flight
+  int kv_end = nk;
+  if (CAUSAL) kv_end = min(nk, min(q0 + kPpBr, q_len));
+  const int n_tiles = (kv_end + T::BC - 1) / T::BC;
+
+  const uint32_t row_bytes = static_cast<uint32_t>(kv_stride) * 2u;
+  auto k_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
+    const int rem16 = c % (16 * (D / 8));
+    *row = 16 * (c / (16 * (D / 8))) + rem16 % 16;
+    *colb = (rem16 / 16) * 16;
+  };
+  auto v_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
+    const int w = c % (D / 2);
+    *row = 4 * (c / (D / 2)) + (w % 8) / 2;
+    *colb = (16 * (w / 8) + 8 * (w % 2)) * 2;
+  };
+  // Group 0 moves V tiles, group 1 K tiles; wave w of a group fills the
+  // 1 KB slot runs (i*4 + w%4)*64 .. +63 of the tile (16 bytes per lane).
+  // Rows past kv_end read as zero (buffer range check) and are masked.
+  const int gw = wave & 3;
+  const bool fetch_v = grp == 0;
+  uint32_t goff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = (i * 4 + gw) * 64 + lane;
+    int row, colb;
+    if (fetch_v) v_slot(c, &row, &colb); else k_slot(c, &row, &colb);
+    goff[i] = row * row_bytes + colb;
+  }
+  const __bf16* gbase = fetch_v ? vbase : kbase;
+  u32x4 stage[CH];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int kv0 = t * T::BC;
+    const int nrows = min(kv_end - kv0, T::BC);
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(gbase + kv0 * kv_stride), (short)0, nrows * (int)row_bytes, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, goff[i], 0, 0));
+  };
+  auto store_chunk = [&](__bf16* dst, auto C) __attribute__((always_inline)) {
+    constexpr int i = decltype(C)::value;
+    *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
+  };
+  auto store_tile = [&](__bf16* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
+  };
+
+  const int k_lane = ((l32 >> 4) * (D / 8) + g) * 128 + (l32 & 15) * 8;
+  const int v_lane = g * T::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
+
+  const float c = p.c;
+  // Tiles crossing the key tail or the diagonal (or lying wholly above this
+  // wave's rows, which the mask then empties) are masked.
+  auto needs_mask = [&](int tile) __attribute__((always_inline)) {
+    const int kv0 = tile * T::BC;
+    return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0);
+  };
+
+  f32x16 sv[T::KT];
+  u32x4 pv_op[T::KT][2];
+  f32x16 acc[T::DT];
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+  for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // ---- MFMA phase: S_j = K_j Q^T (key blocks interleaved), then O += P_{j-1} V_{j-1}.
+  constexpr int kS = T::KT * T::KS;
+  constexpr int kPv = T::KT * 2 * T::DT;
+  constexpr int kAhead = 3;       // LDS operand reads run this many MFMAs ahead
+  constexpr int kMoveFirst = 4;   // tile-store slots inside the MFMA phase
+  constexpr int kMoveStride = 8;
+  static_assert(kMoveFirst + (CH - 1) * kMoveStride < kS + kPv, "move slots");
+  // mid(c) runs after slice kMoveFirst + c*kMoveStride (tile chunk c moves to LDS there).
+  auto mphase = [&](const __bf16* kb, const __bf16* vb, auto&& mid) __attribute__((always_inline)) {
+    constexpr int n0 = kS;          // slices [0, kS): scores; [kS, kS + kPv): P V
+    constexpr int nsl = kS + kPv;
+    auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < n0) {
+        constexpr int kt = i % T::KT, ks = i / T::KT;
+        return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (D / 8) + 2 * ks) * 128);
+      } else {
+        constexpr int s = i - n0;
+        constexpr int kt = s / (2 * T::DT), hh = (s / T::DT) % 2, dt = s % T::DT;
+        const __bf16* p0 = vb + v_lane + (8 * kt + 4 * hh) * T::QUAD + dt * 128;
+        return read_tr_pair(p0, p0 + 2 * T::QUAD);
+      }
+    };
+    bf16x8 opnd[kAhead];
+    static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
+      if constexpr (decltype(I)::value < nsl) opnd[decltype(I)::value] = operand(I);
+    });
+    static_for<0, nsl>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      const bf16x8 a = opnd[i % kAhead];
+      if constexpr (i + kAhead < nsl) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
+      if constexpr (i < n0) {
+        constexpr int kt = i % T::KT, ks = i / T::KT;
+        sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
+      } else {
+        constexpr int s = i - n0;
+        constexpr int kt = s / (2 * T::DT), hh = (s / T::DT) % 2, dt = s % T::DT;
+        acc[dt] = mfma32(a, __builtin_bit_cast(bf16x8, pv_op[kt][hh]), acc[dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i >= kMoveFirst && (i - kMoveFirst) % kMoveStride == 0 &&
+                    (i - kMoveFirst) / kMoveStride < CH) {
+        mid(std::integral_constant<int, (i - kMoveFirst) / kMoveStride>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  };
+  auto apply_mask = [&](int tile) __attribute__((always_inline)) {
+    const int kv0 = tile * T::BC;
+#pragma unroll
+    for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool vis = key < nk && (!CAUSAL || key <= qrow);
+        if (!vis) sv[kt][r] = -INFINITY;
+      }
+  };
+  // ---- VALU phase: online softmax of S_j -> P_j, O rescale when the max moved.
+  auto vphase = [&](int j) __attribute__((always_inline)) {
+    if (needs_mask(j)) apply_mask(j);
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 32; e += 4) {
+      m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
+      m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
+    }
+    const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
+    const bool any = __builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0;
+    const float m_new = any ? fmaxf(m_run, mx) : m_run;
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], c, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
+        ls0 += e0;
+        ls1 += e1;
+        const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+        pv_op[kt][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+      }
+    asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
+    l_run = l_run * alpha + (ls0 + ls1);
+    if (any) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) acc[dt] *= alpha;
+    }
+  };
+
+  // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
+  // V_j at h = 2j+1, group 1 runs M_j at h = 2j+1 and V_j at h = 2j+2.  K_t
+  // lives in k[t%2], V_t in v[t%2].  Tiles move global -> VGPRs -> LDS in
+  // the MFMA phases, between two MFMAs: during M_j group 0 stores V_j
+  // (loaded during M_{j-1}) and loads V_{j+1}; group 1 stores K_{j+1} and
+  // loads K_{j+2}.  Each store is complete before the barrier that ends its
+  // phase, which precedes the first read of the tile.
+  auto kbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
+    if constexpr (decltype(I)::value % 2 == 0) return k_lds0; else return k_lds1;
+  };
+  auto vbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
+    if constexpr (decltype(I)::value % 2 == 0) return v_lds0; else return v_lds1;
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One period: M_j (+ tile store and load), barrier, V_j, barrier.  At j = 0
+  // the P V adds zero (P and the V buffer it reads are zeroed first); at
+  // j = n_tiles the scores come from a stale K tile and are never used.
+  auto period = [&](int j, auto J) __attribute__((always_inline)) {
+    constexpr int j2 = decltype(J)::value;  // j % 2
+    const int st = fetch_v ? j : j + 1;  // tile stored in this phase
+    __bf16* dst = fetch_v ? vbuf(std::integral_constant<int, j2>{}) : kbuf(std::integral_constant<int, j2 + 1>{});
+    // The staged tile goes to LDS one 16-byte chunk per lane at a time,
+    // spread over the phase; after the last chunk the next tile is loaded
+    // into the freed registers.
+    auto move = [&](auto C) __attribute__((always_inline)) {
+      constexpr int c = decltype(C)::value;
+      if (st < n_tiles) {
+        store_chunk(dst, C);
+        if constexpr (c == CH - 1) {
+          if (st + 1 < n_tiles) load_tile(st + 1);
+        }
+      }
+    };
+    mphase(kbuf(std::integral_constant<int, j2>{}), vbuf(std::integral_constant<int, j2 + 1>{}), move);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this phase's LDS stores are done
+    barrier();
+    if (j < n_tiles) vphase(j);
+    barrier();
+  };
+
+#pragma unroll
+  for (int kt = 0; kt < T::KT; ++kt) pv_op[kt][0] = pv_op[kt][1] = u32x4{};
+  for (int i = tid; i < T::V_ELEMS / 8; i += kPpThreads)
+    reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
+  // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
+  if (fetch_v) {
+    if (n_tiles > 0) load_tile(0);
+  } else {
+    if (n_tiles > 0) { load_tile(0); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
+    if (n_tiles > 1) load_tile(1);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  barrier();
+  if (grp == 1) barrier();  // group 1 starts half a period late
+  int j = 0;
+  for (; j + 1 <= n_tiles; j += 2) {
+    period(j, std::integral_constant<int, 0>{});
+    period(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (j <= n_tiles) period(j, std::integral_constant<int, 0>{});
+  if (grp == 0) barrier();
+
+  const float l_tot = pair_sum(l_run);
+  if (qrow < q_len) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* orow = p.o + (q_row0 + qrow) * q_stride + (long)h * D;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * rq + 4 * g) = ov;
+      }
+    if (g == 0)
+      p.lse[lse_base + (long)h * lse_hstride + qrow] =
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 thread_local int g_last_hip_error = 0;
+
+constexpr bool use_pp(int d) { return d == 128; }
 
 template <int D, bool CAUSAL, bool VARLEN>
 int launch_one(const Params& p, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so the check below is ours
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream,
-                     p);
+  if constexpr (use_pp(D))
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kPpThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream,
+                       p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
@@ -585,7 +936,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (B == 0 || Nq == 0) return ATTN_OK;
   rc = check_buffers(q, k, v, o, lse, Nk > 0);
   if (rc != ATTN_OK) return rc;
-  const long nqb = (Nq + kBr - 1) / kBr;
+  const int br = use_pp(d) ? kPpBr : kBr;
+  const long nqb = (Nq + br - 1) / br;
   const long grid = (long)B * Hq * nqb;
   if (grid > INT_MAX || (long)B * Nq > INT_MAX || (long)B * Nk > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
@@ -618,7 +970,8 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
   rc = check_buffers(q, k, v, o, lse, max_seqlen_k > 0);
   if (rc != ATTN_OK) return rc;
-  const long nqb = (max_seqlen_q + kBr - 1) / kBr;
+  const int br = use_pp(d) ? kPpBr : kBr;
+  const long nqb = (max_seqlen_q + br - 1) / br;
   const long grid = (long)num_seqs * Hq * nqb;
   if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
