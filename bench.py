@@ -80,8 +80,12 @@ def make_step(w, x, dev):
         ms = x["max_seqlen"]
         lse = torch.empty((w.Hq, q.shape[0]), dtype=torch.float32, device=dev)
 
-        def step():
-            attn.attn_fwd_varlen(q, k, v, cu, cu, ms, ms, w.scale, w.causal, out=out, lse=lse)
+        plan = torch.empty((cu.numel() - 1,), dtype=torch.int32, device=dev)
+
+        def step():  # LPT plan (FlashAttention-4 summary, section 3.3), then the forward
+            attn.attn_varlen_plan(cu, cu, ms, ms, w.causal, out=plan)
+            attn.attn_fwd_varlen(q, k, v, cu, cu, ms, ms, w.scale, w.causal, out=out, lse=lse,
+                                 seq_order=plan)
     else:
         sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)

@@ -30,7 +30,8 @@ ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_strerror", "attn_last_hip_error", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_varlen_plan", "attn_strerror", "attn_last_hip_error",
+           "attn_version")
 
 _lib = None
 
@@ -48,8 +49,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.attn_fwd.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
-                                    i32, vp]
+                                    i32, vp, vp]
     lib.attn_fwd_varlen.restype = i32
+    lib.attn_varlen_plan.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.attn_varlen_plan.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -142,12 +145,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
 def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                     scale: Optional[float] = None, causal: bool = False,
-                    out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    seq_order: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Packed forward: q [Tq,Hq,d], k/v [Tk,Hkv,d], cu_seqlens int32 [S+1] on the GPU.
 
     Returns O bf16 [Tq,Hq,d] and LSE fp32 [Hq,Tq].  Rows of a freshly allocated
-    O / LSE that belong to no sequence are left as zero.
+    O / LSE that belong to no sequence are left as zero.  seq_order (int32 [S],
+    from attn_varlen_plan) sets the order in which sequences are scheduled.
     """
     lib = load_library()
     _need(q, "q", torch.bfloat16)
@@ -165,6 +169,10 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of equal length")
     num_seqs = cu_seqlens_q.numel() - 1
+    if seq_order is not None:
+        _need(seq_order, "seq_order", torch.int32, dev)
+        if seq_order.shape != (num_seqs,):
+            raise ValueError("seq_order must have shape [num_seqs]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -182,6 +190,29 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     rc = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                              _ptr(cu_seqlens_k), num_seqs, Hq, Hkv, int(max_seqlen_q),
                              int(max_seqlen_k), d, float(scale), int(bool(causal)),
-                             _stream_handle(dev))
+                             _ptr(seq_order), _stream_handle(dev))
     _check(rc, "attn_fwd_varlen")
     return out, lse
+
+
+def attn_varlen_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                     max_seqlen_k: int, causal: bool = False,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Longest-first sequence order (int32 [S]) for attn_fwd_varlen's seq_order."""
+    lib = load_library()
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    dev = cu_seqlens_q.device
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of equal length")
+    num_seqs = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((num_seqs,), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", torch.int32, dev)
+        if out.shape != (num_seqs,):
+            raise ValueError("out must have shape [num_seqs]")
+    rc = lib.attn_varlen_plan(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q),
+                              int(max_seqlen_k), int(bool(causal)), _ptr(out), _stream_handle(dev))
+    _check(rc, "attn_varlen_plan")
+    return out

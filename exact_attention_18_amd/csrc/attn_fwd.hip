@@ -49,13 +49,15 @@
 //   score; LSE is converted back to natural log in the epilogue.
 // * Causal: key blocks past the query block's last row are never visited;
 //   masks are applied only on blocks that cross the diagonal or the key tail.
-// * Grid order: workgroup ids are assigned round-robin to the 8 XCDs, so the
-//   id is first remapped to make each XCD's share a contiguous run of logical
-//   work items; logical order is batch, KV head, query block (longest first
-//   under the causal mask), then the query heads sharing that KV head, so the
-//   workgroups resident on one XCD read the same K/V from its L2
-//   (longest-processing-time-first scheduling and head grouping of
-//   FlashAttention-4 (papercache summary), section 3.3).
+// * Grid order (decode_work): (batch or sequence, KV head) units are dealt
+//   round-robin to the 8 XCDs, each XCD running its units one after another,
+//   query blocks longest first under the causal mask and the query heads of
+//   the KV group innermost.  The workgroups resident on one XCD thus read the
+//   same K/V from its L2, and every XCD gets a like share of every batch
+//   element.  Packed batches can also be taken in the longest-first sequence
+//   order written by varlen_plan_kernel (longest-processing-time-first
+//   scheduling, head grouping and the varlen batch map of FlashAttention-4
+//   (papercache summary), section 3.3).
 //
 // Two kernels
 // -----------
@@ -125,12 +127,45 @@ struct Params {
   const int32_t* seqlens_k;  // padded form, may be null
   const int32_t* cu_q;       // packed form
   const int32_t* cu_k;
+  const int32_t* seq_order;  // packed form: virtual -> actual sequence, may be null
   int Hq, Hkv, G;
   int Nq, Nk;  // packed form: max_seqlen_q, max_seqlen_k
   int nqb;     // query blocks per (sequence, head)
   int num_seqs;
   float c;  // scale * log2(e)
 };
+
+// Work decode.  A unit is one (batch element or sequence, KV head) pair,
+// u = b * Hkv + hkv.  Units are dealt round-robin to the 8 XCDs (the hardware
+// sends workgroup id w to XCD w % 8): XCD x runs units x, x+8, x+16, ... in
+// that order, each unit's items back to back -- query blocks longest first
+// under the causal mask, the query heads of the KV group innermost.  So the
+// workgroups resident on one XCD stream the same K/V through its L2, and every
+// XCD gets a like share of every batch element, also when their lengths
+// differ (longest-processing-time-first order of FlashAttention-4
+// (papercache summary), section 3.3).  The grid holds ceil(units / 8) * 8
+// units; ids past the last unit are padding.
+struct WorkItem {
+  int b, hkv, qb, gi;
+  bool valid;
+};
+
+__device__ __forceinline__ WorkItem decode_work(const Params& p, bool causal) {
+  const int units = p.num_seqs * p.Hkv;
+  const int per_unit = p.nqb * p.G;
+  const int x = blockIdx.x % kXcds;
+  const int r = blockIdx.x / kXcds;
+  const int u = (r / per_unit) * kXcds + x;
+  const int item = r % per_unit;
+  const int qbi = item / p.G;
+  WorkItem w;
+  w.valid = u < units;
+  w.b = u / p.Hkv;
+  w.hkv = u % p.Hkv;
+  w.gi = item % p.G;
+  w.qb = causal ? (p.nqb - 1 - qbi) : qbi;
+  return w;
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -194,20 +229,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // ---- work item: XCD-contiguous remap, then (seq, kv head, q block, head in group)
-  const int n = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int per = n / kXcds;
-  const int rem = n % kXcds;
-  int t = xcd * per + min(xcd, rem) + bid / kXcds;
-  const int gi = t % p.G;
-  t /= p.G;
-  const int qbi = t % p.nqb;
-  t /= p.nqb;
-  const int hkv = t % p.Hkv;
-  const int b = t / p.Hkv;
-  const int qb = CAUSAL ? (p.nqb - 1 - qbi) : qbi;
+  // ---- work item (see decode_work)
+  const WorkItem wi = decode_work(p, CAUSAL);
+  if (!wi.valid) return;  // grid padding; uniform over the workgroup
+  const int b = (VARLEN && p.seq_order != nullptr)
+                    ? min(max(p.seq_order[wi.b], 0), p.num_seqs - 1)
+                    : wi.b;
+  const int hkv = wi.hkv, qb = wi.qb, gi = wi.gi;
   const int h = hkv * p.G + gi;
 
   int q_len, nk;
@@ -571,19 +599,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const int n = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int per = n / kXcds;
-  const int rem = n % kXcds;
-  int t = xcd * per + min(xcd, rem) + bid / kXcds;
-  const int gi = t % p.G;
-  t /= p.G;
-  const int qbi = t % p.nqb;
-  t /= p.nqb;
-  const int hkv = t % p.Hkv;
-  const int b = t / p.Hkv;
-  const int qb = CAUSAL ? (p.nqb - 1 - qbi) : qbi;
+  // ---- work item (see decode_work)
+  const WorkItem wi = decode_work(p, CAUSAL);
+  if (!wi.valid) return;  // grid padding; uniform over the workgroup
+  const int b = (VARLEN && p.seq_order != nullptr)
+                    ? min(max(p.seq_order[wi.b], 0), p.num_seqs - 1)
+                    : wi.b;
+  const int hkv = wi.hkv, qb = wi.qb, gi = wi.gi;
   const int h = hkv * p.G + gi;
 
   int q_len, nk;
@@ -873,6 +895,54 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// LPT order of the sequences of a packed batch (FlashAttention-4 (papercache
+// summary), section 3.3): a counting sort, in one workgroup, of the sequences
+// by the key-tile count of their longest work tile, longest first.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 8192;          // keys >= kPlanBuckets - 1 share the top bucket
+constexpr int kPlanPer = kPlanBuckets / kPlanThreads;
+
+__global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(const int32_t* cu_q,
+                                                                    const int32_t* cu_k, int n,
+                                                                    int max_q, int max_k,
+                                                                    int causal, int32_t* order) {
+  __shared__ int hist[kPlanBuckets];
+  __shared__ int part[kPlanThreads];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPlanBuckets; i += kPlanThreads) hist[i] = 0;
+  __syncthreads();
+  auto key = [&](int z) {
+    const int lq = min(max(cu_q[z + 1] - cu_q[z], 0), max_q);
+    const int lk = min(max(cu_k[z + 1] - cu_k[z], 0), max_k);
+    const int w = causal ? min(lq, lk) : lk;
+    return min((w + 63) / 64, kPlanBuckets - 1);
+  };
+  for (int z = tid; z < n; z += kPlanThreads) atomicAdd(&hist[key(z)], 1);
+  __syncthreads();
+  // Exclusive scan in descending key order: thread t owns the kPlanPer
+  // buckets counted from the top, (kPlanBuckets-1 - t*kPlanPer) downwards.
+  int sum = 0;
+  for (int i = 0; i < kPlanPer; ++i) sum += hist[kPlanBuckets - 1 - (tid * kPlanPer + i)];
+  part[tid] = sum;
+  __syncthreads();
+  for (int step = 1; step < kPlanThreads; step *= 2) {
+    const int add = tid >= step ? part[tid - step] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;  // buckets of higher key than this thread's first
+  for (int i = 0; i < kPlanPer; ++i) {
+    const int kb = kPlanBuckets - 1 - (tid * kPlanPer + i);
+    const int c = hist[kb];
+    hist[kb] = run;  // becomes the next free position of bucket kb
+    run += c;
+  }
+  __syncthreads();
+  for (int z = tid; z < n; z += kPlanThreads) order[atomicAdd(&hist[key(z)], 1)] = z;
+}
+
 thread_local int g_last_hip_error = 0;
 
 constexpr bool use_pp(int d) { return d == 128; }
@@ -907,6 +977,10 @@ int dispatch(const Params& p, int d, bool causal, bool varlen, int grid, hipStre
                 : launch_one<128, false, false>(p, grid, stream);
 }
 
+// Workgroups for `units` (batch, KV head) units of `per_unit` items each,
+// units padded to a multiple of the XCD count (decode_work).
+long grid_size(long units, long per_unit) { return (units + kXcds - 1) / kXcds * kXcds * per_unit; }
+
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 int check_common(int Hq, int Hkv, int d, float scale) {
@@ -938,7 +1012,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (rc != ATTN_OK) return rc;
   const int br = use_pp(d) ? kPpBr : kBr;
   const long nqb = (Nq + br - 1) / br;
-  const long grid = (long)B * Hq * nqb;
+  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv));
   if (grid > INT_MAX || (long)B * Nq > INT_MAX || (long)B * Nk > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
   p.q = static_cast<const __bf16*>(q);
@@ -962,7 +1036,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
 extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                int num_seqs, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k,
-                               int d, float scale, int causal, void* stream) {
+                               int d, float scale, int causal, const int32_t* seq_order,
+                               void* stream) {
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_SIZE;
   int rc = check_common(Hq, Hkv, d, scale);
   if (rc != ATTN_OK) return rc;
@@ -972,7 +1047,7 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   if (rc != ATTN_OK) return rc;
   const int br = use_pp(d) ? kPpBr : kBr;
   const long nqb = (max_seqlen_q + br - 1) / br;
-  const long grid = (long)num_seqs * Hq * nqb;
+  const long grid = grid_size((long)num_seqs * Hkv, (long)nqb * (Hq / Hkv));
   if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
   p.q = static_cast<const __bf16*>(q);
@@ -982,6 +1057,7 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   p.lse = lse;
   p.cu_q = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
+  p.seq_order = seq_order;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
@@ -992,6 +1068,25 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   return dispatch(p, d, causal != 0, true, static_cast<int>(grid),
                   static_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int num_seqs, int max_seqlen_q, int max_seqlen_k, int causal,
+                                int32_t* seq_order, void* stream) {
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_SIZE;
+  if (num_seqs == 0) return ATTN_OK;
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr || seq_order == nullptr)
+    return ATTN_ERR_NULL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0,
+                     static_cast<hipStream_t>(stream), cu_seqlens_q, cu_seqlens_k, num_seqs,
+                     max_seqlen_q, max_seqlen_k, causal != 0 ? 1 : 0, seq_order);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
 }
 
 extern "C" const char* attn_strerror(int status) {

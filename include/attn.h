@@ -102,11 +102,41 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
  * (FlashAttention notes (xwysyy), code-structure overview, the "unpadded"
  * interface; FlashAttention-4 (papercache summary), section 3.3, varlen
  * metadata held on the device).
+ * seq_order is NULL (sequences in index order) or a device int32 [num_seqs]
+ * permutation from attn_varlen_plan: workgroups then take the sequences in
+ * that order (out-of-range entries are clamped, never read out of bounds).
+ * The order changes only the schedule, never a result.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
                     int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
-                    int causal, void* stream);
+                    int causal, const int32_t* seq_order, void* stream);
+
+/*
+ * Longest-processing-time-first order of the sequences of a packed batch
+ * ("FlashAttention-4" (papercache summary), section 3.3, LPT for variable
+ * sequence lengths: a preprocessing kernel sorts the batches by the running
+ * time of their longest work tile and writes a virtual-to-actual batch index
+ * map that the attention kernel reads back; the map can be cached).
+ *   cu_seqlens_q, cu_seqlens_k : device int32 [num_seqs + 1], as for
+ *               attn_fwd_varlen.
+ *   max_seqlen_q, max_seqlen_k : the same bounds attn_fwd_varlen receives.
+ *   causal    : the mask the forward will use (it changes the sort key).
+ *   seq_order : device int32 [num_seqs], written: seq_order[v] is the
+ *               sequence the forward processes v-th.  It is a permutation of
+ *               0 .. num_seqs-1 in non-increasing order of the key
+ *               ceil(w / 64), w = min(lq, lk) keys under the causal mask,
+ *               lk otherwise (lq, lk: the sequence's lengths clamped to the
+ *               max_seqlen bounds); the order among equal keys is
+ *               unspecified and does not change any output of the forward.
+ * Pass seq_order to attn_fwd_varlen (NULL there means sequence order).
+ * num_seqs == 0 is a no-op.  Asynchronous on stream; allocates nothing.
+ * Returns an attn_status (ATTN_ERR_NULL for a NULL pointer with num_seqs > 0,
+ * ATTN_ERR_SIZE for negative sizes).
+ */
+int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
+                     int max_seqlen_q, int max_seqlen_k, int causal, int32_t* seq_order,
+                     void* stream);
 
 /* Static text for an attn_status code (never NULL). */
 const char* attn_strerror(int status);

@@ -56,7 +56,30 @@ def _varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cq=FAKE, ck=FAKE, S=3, Hq=
     lib = attn.load_library()
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.attn_fwd_varlen(vp(q), vp(k), vp(v), vp(o), vp(lse), vp(cq), vp(ck), S, Hq, Hkv,
-                               mq, mk, d, scale, causal, None)
+                               mq, mk, d, scale, causal, None, None)
+
+
+def _plan(cq=FAKE, ck=FAKE, S=3, mq=100, mk=100, causal=1, order=FAKE):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_varlen_plan(vp(cq), vp(ck), S, mq, mk, causal, vp(order), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), attn.ATTN_ERR_NULL),
+    (dict(ck=None), attn.ATTN_ERR_NULL),
+    (dict(order=None), attn.ATTN_ERR_NULL),
+    (dict(S=-1), attn.ATTN_ERR_SIZE),
+    (dict(mq=-1), attn.ATTN_ERR_SIZE),
+    (dict(mk=-2), attn.ATTN_ERR_SIZE),
+])
+def test_attn_varlen_plan_rejects_bad_arguments(kw, code):
+    assert _plan(**kw) == code
+
+
+def test_attn_varlen_plan_empty_is_a_noop():
+    # nothing is launched, so even NULL pointers are fine
+    assert _plan(S=0, cq=None, ck=None, order=None) == attn.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -109,6 +109,56 @@ def test_varlen_separate_key_lengths():
         assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "varlen lq != lk")
 
 
+def _plan_keys(lq, lk, mq, mk, causal):
+    """Sort key of the LPT plan, from its definition: key tiles of the longest work tile."""
+    lq = np.minimum(np.maximum(lq, 0), mq)
+    lk = np.minimum(np.maximum(lk, 0), mk)
+    w = np.minimum(lq, lk) if causal else lk
+    return np.minimum((w + 63) // 64, 8191)
+
+
+@pytest.mark.parametrize("case", ["mixed", "many", "equal"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_plan_orders_sequences_longest_first(case, causal):
+    rng = np.random.default_rng(8600 + len(case) + int(causal))
+    if case == "mixed":
+        lq = np.array([1, 130, 257, 0, 64, 200, 5000, 63, 64, 65], dtype=np.int64)
+        lk = np.array([300, 17, 257, 9, 0, 4096, 70, 63, 64, 700], dtype=np.int64)
+    elif case == "many":
+        lq = rng.integers(0, 2000, size=3000)
+        lk = rng.integers(0, 2000, size=3000)
+    else:
+        lq = np.full(1500, 777)
+        lk = np.full(1500, 777)
+    mq, mk = int(lq.max()), int(lk.max())
+    cq = inputs.cu_from_lengths(torch.tensor(lq, dtype=torch.int32)).to(DEV)
+    ck = inputs.cu_from_lengths(torch.tensor(lk, dtype=torch.int32)).to(DEV)
+    print(f"[parity] varlen plan {case} causal={causal} n={len(lq)}", flush=True)
+    order = attn.attn_varlen_plan(cq, ck, mq, mk, causal).cpu().numpy()
+    assert sorted(order.tolist()) == list(range(len(lq))), "not a permutation"
+    keys = _plan_keys(lq, lk, mq, mk, causal)[order]
+    assert (np.diff(keys) <= 0).all(), "keys increase somewhere"
+
+
+def test_varlen_plan_changes_no_output():
+    lengths = torch.tensor([1, 130, 257, 0, 64, 200, 700, 3], dtype=torch.int32)
+    cu = inputs.cu_from_lengths(lengths).to(DEV)
+    T, ms = int(lengths.sum()), int(lengths.max())
+    for causal, d, (Hq, Hkv) in [(True, 128, (4, 2)), (False, 64, (4, 4))]:
+        q, k, v = inputs.make_packed_qkv(T, T, Hq, Hkv, d, 8700 + d)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        scale = 1.0 / math.sqrt(d)
+        plan = attn.attn_varlen_plan(cu, cu, ms, ms, causal)
+        o1, l1 = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, ms, ms, scale, causal)
+        o2, l2 = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, ms, ms, scale, causal, seq_order=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        o_ref, lse_ref = oracle.attention_forward_varlen(to_np64(q), to_np64(k), to_np64(v),
+                                                         cu.cpu().numpy(), cu.cpu().numpy(), scale,
+                                                         causal)
+        assert_parity(errors(to_np64(o2), to_np64(l2), o_ref, lse_ref), "varlen with plan")
+
+
 def test_outputs_are_not_overrun():
     """O and LSE written inside their buffers only (sentinels around both)."""
     B, N, Hq, Hkv, d = 2, 333, 4, 2, 128
@@ -163,7 +213,10 @@ def test_full_workload_sampled_rows(name):
         cu = x["cu_seqlens_q"].to(DEV)
         ms = x["max_seqlen"]
         o, lse = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, ms, ms, w.scale, w.causal)
-        o2, lse2 = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, ms, ms, w.scale, w.causal)
+        # the benchmark's launch: longest-first sequence order from the plan
+        plan = attn.attn_varlen_plan(cu, cu, ms, ms, w.causal)
+        o2, lse2 = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, ms, ms, w.scale, w.causal,
+                                        seq_order=plan)
     else:
         sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(DEV)
         o, lse = attn.attn_fwd(qd, kd, vd, w.scale, w.causal, sl)
