@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for the fused exact-attention forward.
+"""CPU fp64 oracle for the fused exact-attention forward and backward.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -6,7 +6,8 @@ and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
 the HIP path (``exact_attention_18_amd``) and imports nothing from it; the two
 meet only at the seeded input tensors.
 
-Every function is pinned by ``tests/test_oracle.py`` to facts the pages and the
+Every function is pinned by ``tests/test_oracle.py`` (forward) and
+``tests/test_oracle_backward.py`` (backward) to facts the pages and the
 mathematics fix (worked example, closed forms, invariants, a library routine of
 the same definition, brute force).  No function here is "parity unpinned".
 """
@@ -18,4 +19,11 @@ from .attention import (  # noqa: F401
     attention_forward_varlen,
     attention_rows,
     online_softmax_head,
+)
+from .backward import (  # noqa: F401,E402
+    attention_backward,
+    attention_backward_head,
+    attention_backward_varlen,
+    blockwise_backward_head,
+    softmax_backward_delta,
 )
