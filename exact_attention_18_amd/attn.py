@@ -30,8 +30,8 @@ ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_varlen_plan", "attn_strerror", "attn_last_hip_error",
-           "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_varlen_plan", "attn_bwd", "attn_bwd_workspace_size",
+           "attn_strerror", "attn_last_hip_error", "attn_version")
 
 _lib = None
 
@@ -53,6 +53,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_varlen.restype = i32
     lib.attn_varlen_plan.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     lib.attn_varlen_plan.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                             f32, i32, vp, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -216,3 +221,57 @@ def attn_varlen_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max
                               int(max_seqlen_k), int(bool(causal)), _ptr(out), _stream_handle(dev))
     _check(rc, "attn_varlen_plan")
     return out
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+             seqlens_k: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None,
+             out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV (bf16) of the batched forward from its O and LSE and the upstream dO.
+
+    Layouts as in attn_fwd; d must be 128.  The workspace (uint8, at least
+    attn_bwd_workspace_size bytes) is allocated here when not given.
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("expected q, o, dout [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d]")
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk_ = k.shape
+    if Bk != B or dk_ != d:
+        raise ValueError("q and k disagree on batch or head dim")
+    if lse.shape != (B, Hq, Nq):
+        raise ValueError("lse must have shape [B,Hq,Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if seqlens_k is not None:
+        _need(seqlens_k, "seqlens_k", torch.int32, dev)
+        if seqlens_k.shape != (B,):
+            raise ValueError("seqlens_k must have shape [B]")
+    need = int(lib.attn_bwd_workspace_size(B, Hq, Nq))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _need(dq, "dq", torch.bfloat16, dev)
+        _need(dk, "dk", torch.bfloat16, dev)
+        _need(dv, "dv", torch.bfloat16, dev)
+        if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
+            raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    rc = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                      _ptr(dv), _ptr(workspace), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                      int(bool(causal)), _ptr(seqlens_k), _stream_handle(dev))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv

@@ -81,23 +81,14 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "cdna4.h"
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
-constexpr int kXcds = 8;                    // MI355X: 8 XCDs, 32 CUs each
-constexpr float kLn2 = 0.693147180559945309f;
 
 template <int D>
 struct Tile {
@@ -112,11 +103,7 @@ struct Tile {
   static_assert(CHUNKS * kThreads * 8 == BC * D, "tile split");
 };
 
-constexpr int kWaitVm0 = 0;  // s_waitcnt immediate: every counter zero
-// s_waitcnt lgkmcnt(0) only (gfx9 encoding: vmcnt 63, expcnt 7).
-constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
 constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
-constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 
 struct Params {
   const __bf16* q;
@@ -165,51 +152,6 @@ __device__ __forceinline__ WorkItem decode_work(const Params& p, bool causal) {
   w.gi = item % p.G;
   w.qb = causal ? (p.nqb - 1 - qbi) : qbi;
   return w;
-}
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// max(a, b, c) in one instruction.  fmaxf would make the compiler quiet
-// possible signalling NaNs of the MFMA results first (an extra instruction per
-// operand); scores here are finite or -inf.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Reductions over the lane pair (l, l^32).  v_permlane32_swap exchanges the
-// upper half-wave of one register with the lower half-wave of another; with
-// x in both, every lane ends up holding x_l in one result and x_(l^32) in the
-// other, so a symmetric combine of the two needs no lane select.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), -INFINITY);
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Two transpose reads of LDS, concatenated into one 8-element bf16 operand.
-__device__ __forceinline__ bf16x8 read_tr_pair(const __bf16* p0, const __bf16* p1) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-  const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -943,7 +885,6 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(const int32_t
   for (int z = tid; z < n; z += kPlanThreads) order[atomicAdd(&hist[key(z)], 1)] = z;
 }
 
-thread_local int g_last_hip_error = 0;
 
 constexpr bool use_pp(int d) { return d == 128; }
 
@@ -958,7 +899,7 @@ int launch_one(const Params& p, int grid, hipStream_t stream) {
                        p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_last_hip_error = static_cast<int>(e);
+    attn_detail::last_hip_error = static_cast<int>(e);
     return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
@@ -1083,7 +1024,7 @@ extern "C" int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_s
                      max_seqlen_q, max_seqlen_k, causal != 0 ? 1 : 0, seq_order);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_last_hip_error = static_cast<int>(e);
+    attn_detail::last_hip_error = static_cast<int>(e);
     return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
@@ -1103,6 +1044,6 @@ extern "C" const char* attn_strerror(int status) {
   }
 }
 
-extern "C" int attn_last_hip_error(void) { return g_last_hip_error; }
+extern "C" int attn_last_hip_error(void) { return attn_detail::last_hip_error; }
 
 extern "C" const char* attn_version(void) { return "0.1.0"; }

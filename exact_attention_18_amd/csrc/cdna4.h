@@ -1,0 +1,82 @@
+// Device helpers for CDNA4 (gfx950) shared by the attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+// hipError_t of the last failed launch on this thread, shared by every entry point.
+namespace attn_detail {
+inline thread_local int last_hip_error = 0;
+}  // namespace attn_detail
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, 32 CUs each; workgroup id w runs on XCD w % 8
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaitVm0 = 0;  // s_waitcnt immediate: every counter zero
+// s_waitcnt lgkmcnt(0) only (gfx9 encoding: vmcnt 63, expcnt 7).
+constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
+
+// v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] B[16x32].  Operand layout:
+// lane l holds row (A) or column (B) l%32 and the 8 k-elements 8*(l/32)..+7;
+// the accumulator: lane l holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4
+// in register r.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max(a, b, c) in one instruction.  fmaxf would make the compiler quiet
+// possible signalling NaNs of the MFMA results first (an extra instruction per
+// operand); scores here are finite or -inf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Reductions over the lane pair (l, l^32).  v_permlane32_swap exchanges the
+// upper half-wave of one register with the lower half-wave of another; with
+// x in both, every lane ends up holding x_l in one result and x_(l^32) in the
+// other, so a symmetric combine of the two needs no lane select.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), -INFINITY);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Two transpose reads of LDS, concatenated into one 8-element bf16 operand.
+__device__ __forceinline__ bf16x8 read_tr_pair(const __bf16* p0, const __bf16* p1) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+}  // namespace

@@ -95,6 +95,12 @@ def make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=1.0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_dout(shape, seed):
+    """Upstream gradient dO of the given shape: i.i.d. N(0,1) rounded once to bf16."""
+    g = torch.Generator().manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
 def make_packed_qkv(total_q, total_k, Hq, Hkv, d, seed, q_mult=1.0):
     """Packed Q [Tq,Hq,d], K [Tk,Hkv,d], V [Tk,Hkv,d] as bf16 CPU tensors."""
     g = torch.Generator().manual_seed(int(seed))

@@ -32,13 +32,15 @@
  *   packed (varlen) form:
  *     q, o : bf16 [Tq, Hq, d]           k, v : bf16 [Tk, Hkv, d]
  *     lse  : fp32 [Hq, Tq],             Tq = cu_seqlens_q[num_seqs]
- * d must be 64 or 128.  q, k, v and o must be 16-byte aligned; lse 4-byte.
+ * d must be 64 or 128 (128 for the backward).  q, k, v and o must be
+ * 16-byte aligned; lse 4-byte.
  * O is rounded to bf16 (round-to-nearest-even); LSE stays fp32.
  *
  * Memory and ownership.  Every pointer (q, k, v, o, lse, seqlens_k,
- * cu_seqlens_*) is a DEVICE pointer owned by the caller.  The library
- * allocates nothing, keeps no state besides a thread-local copy of the last
- * HIP error, and is re-entrant.  o and lse must not overlap the inputs or each
+ * cu_seqlens_*, and the backward's dout, dq, dk, dv, workspace) is a DEVICE
+ * pointer owned by the caller.  The library allocates nothing, keeps no
+ * state besides a thread-local copy of the last HIP error, and is
+ * re-entrant.  o and lse must not overlap the inputs or each
  * other.  All calls are asynchronous on `stream` (a hipStream_t; NULL means
  * the default stream): they return after the launch and never synchronise.
  *
@@ -54,6 +56,7 @@
 #ifndef EXACT_ATTENTION_18_AMD_ATTN_H
 #define EXACT_ATTENTION_18_AMD_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -137,6 +140,42 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
                      int max_seqlen_q, int max_seqlen_k, int causal, int32_t* seq_order,
                      void* stream);
+
+/*
+ * Backward pass of the batched forward above (FlashAttention-4 (papercache
+ * summary), section 2.1, the backward equations; "059 · FlashAttention"
+ * (wq-win), section 3, recomputation from the saved row statistics):
+ *     dV = P^T dO,  dP = dO V^T,  dS = (diag(p) - p p^T) dp row-wise,
+ *     dQ = scale dS K,  dK = scale dS^T Q,
+ * where P = exp(S - LSE) is rebuilt from the forward's LSE.  The gradient of a
+ * KV head sums over its G = Hq / Hkv query heads.  Masks, GQA map, layouts
+ * and `seqlens_k` are those of attn_fwd; keys past seqlens_k[b] get zero
+ * gradient.
+ *   q, k, v, seqlens_k, scale, causal : exactly as passed to attn_fwd.
+ *   o, lse    : the forward's outputs for these inputs (bf16 [B,Nq,Hq,d] and
+ *               fp32 [B,Hq,Nq], natural log).
+ *   dout      : bf16 [B,Nq,Hq,d], gradient of the loss with respect to O.
+ *   dq        : bf16 [B,Nq,Hq,d], written in full.
+ *   dk, dv    : bf16 [B,Nk,Hkv,d], written in full (every key of every KV head).
+ *   workspace : device memory of attn_bwd_workspace_size(B, Hq, Nq) bytes,
+ *               16-byte aligned, owned by the caller; its contents on entry do
+ *               not matter and on return are unspecified.  Calls that overlap
+ *               on the GPU need separate workspaces.
+ *   d         : 128 (the only head dimension of the backward kernels).
+ * Results are deterministic: every dQ row is summed inside one workgroup and
+ * every dK / dV row likewise, with no atomic adds.  Asynchronous on stream;
+ * allocates nothing.  Returns an attn_status (ATTN_ERR_HEAD_DIM for d != 128;
+ * ATTN_ERR_NULL / ATTN_ERR_ALIGN as for attn_fwd, including the workspace).
+ * B == 0, or Nq == 0 and Nk == 0, is a no-op.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
+             void* stream);
+
+/* Bytes of workspace attn_bwd needs: two fp32 per (batch, query head, query
+ * row); 0 when any argument is <= 0. */
+size_t attn_bwd_workspace_size(int B, int Hq, int Nq);
 
 /* Static text for an attn_status code (never NULL). */
 const char* attn_strerror(int status);

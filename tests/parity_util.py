@@ -60,3 +60,26 @@ def sample_rows(rng, B, H, N, n, block=128):
         i = special[t] if t < len(special) else int(rng.integers(N))
         out.append((b, h, i))
     return out
+
+
+# Backward tolerance, derived from the arithmetic (no value is stated for the
+# backward): every product in a gradient has one operand rounded to bf16 (P or
+# dS, relative error <= 2^-9) and every gradient is rounded to bf16 on output
+# (<= 2^-9 relative), so the expected relative Frobenius error is about
+# sqrt(2) * 2^-9 = 2.8e-3; the bars below leave a factor ~3.5 (Frobenius) and
+# one bf16 ulp at the largest magnitude plus accumulation (max abs).
+GRAD_REL_FRO = 1e-2
+GRAD_MAX_REL = 2e-2
+
+
+def grad_errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = max(np.abs(ref).max(), 1e-30)
+    return {"rel_fro": float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)),
+            "max_rel": float(np.abs(got - ref).max() / scale)}
+
+
+def assert_grad_parity(errs, what):
+    assert errs["rel_fro"] <= GRAD_REL_FRO, f"{what}: {errs}"
+    assert errs["max_rel"] <= GRAD_MAX_REL, f"{what}: {errs}"

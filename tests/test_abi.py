@@ -155,3 +155,52 @@ def test_binding_refuses_cpu_tensors():
 def test_missing_library_is_an_error(tmp_path):
     with pytest.raises(RuntimeError):
         attn.load_library(str(tmp_path / "nope.so"))
+
+
+def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
+         B=2, Hq=4, Hkv=2, Nq=256, Nk=256, d=128, scale=0.088, causal=1, seqlens=None):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_bwd(vp(q), vp(k), vp(v), vp(o), vp(lse), vp(do), vp(dq), vp(dk), vp(dv), vp(ws),
+                        B, Hq, Hkv, Nq, Nk, d, scale, causal, vp(seqlens), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(k=None), attn.ATTN_ERR_NULL),
+    (dict(o=None), attn.ATTN_ERR_NULL),
+    (dict(lse=None), attn.ATTN_ERR_NULL),
+    (dict(do=None), attn.ATTN_ERR_NULL),
+    (dict(dq=None), attn.ATTN_ERR_NULL),
+    (dict(dk=None), attn.ATTN_ERR_NULL),
+    (dict(dv=None), attn.ATTN_ERR_NULL),
+    (dict(ws=None), attn.ATTN_ERR_NULL),
+    (dict(d=64), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_HEADS),
+    (dict(Hkv=0), attn.ATTN_ERR_HEADS),
+    (dict(B=-1), attn.ATTN_ERR_SIZE),
+    (dict(Nq=-1), attn.ATTN_ERR_SIZE),
+    (dict(scale=float("nan")), attn.ATTN_ERR_SIZE),
+    (dict(scale=0.0), attn.ATTN_ERR_SIZE),
+    (dict(ws=FAKE + 8), attn.ATTN_ERR_ALIGN),
+    (dict(dq=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(dv=FAKE + 4), attn.ATTN_ERR_ALIGN),
+    (dict(lse=FAKE + 2), attn.ATTN_ERR_ALIGN),
+])
+def test_attn_bwd_rejects_bad_arguments(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_attn_bwd_empty_problem_is_a_noop():
+    assert _bwd(B=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+                ws=None) == attn.ATTN_OK
+    assert _bwd(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None,
+                dv=None, ws=None) == attn.ATTN_OK
+
+
+def test_attn_bwd_workspace_size():
+    lib = attn.load_library()
+    assert lib.attn_bwd_workspace_size(2, 4, 100) == 2 * 4 * 2 * 4 * 100
+    assert lib.attn_bwd_workspace_size(0, 4, 100) == 0
+    assert lib.attn_bwd_workspace_size(3, -1, 100) == 0

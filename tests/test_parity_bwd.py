@@ -1,0 +1,103 @@
+"""GPU parity of the backward pass against the fp64 CPU oracle.
+
+The backward consumes the GPU forward's own O and LSE (as in training), and a
+seeded upstream gradient dO.  Small shapes are compared on every element of
+dQ, dK and dV; they span several key and query tiles, ragged tails,
+Nq != Nk, GQA groups and key padding.  At the benchmark's size one whole
+(batch, KV head) slice -- its query heads' dQ and the KV head's dK, dV -- is
+compared element by element.  Tolerances are derived in parity_util.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_18_amd import attn, inputs
+from parity_util import assert_grad_parity, grad_errors, to_np64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+SMALL = [
+    # B, Nq, Nk, Hq, Hkv, causal, padded
+    (1, 64, 64, 1, 1, False, False),
+    (2, 200, 200, 4, 2, True, False),
+    (1, 130, 517, 2, 1, False, False),
+    (1, 517, 130, 2, 2, True, False),
+    (2, 333, 333, 8, 2, True, True),
+    (3, 257, 257, 2, 2, False, True),
+    (1, 1, 1, 1, 1, True, False),
+    (1, 300, 45, 4, 1, True, False),
+]
+
+
+def _fwd_bwd(q, k, v, do, scale, causal, seqlens):
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    sl = None if seqlens is None else seqlens.to(DEV)
+    o, lse = attn.attn_fwd(qd, kd, vd, scale, causal, sl)
+    dq, dk, dv = attn.attn_bwd(qd, kd, vd, o, lse, dod, scale, causal, sl)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal,padded", SMALL)
+def test_backward_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded):
+    d = 128
+    seed = 9000 + B * 31 + Nq * 7 + Nk + Hq * 3 + int(causal)
+    q, k, v = inputs.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=2.0)
+    do = inputs.make_dout(q.shape, seed + 1)
+    seqlens = None
+    if padded:
+        seqlens = inputs.make_seqlens(B, 0, Nk, seed + 2)
+        seqlens[0] = 0
+        if B > 1:
+            seqlens[1] = Nk
+    scale = 1.0 / math.sqrt(d)
+    print(f"[parity-bwd] B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} causal={causal} padded={padded}",
+          flush=True)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, scale, causal, seqlens)
+    rq, rk, rv = oracle.attention_backward(to_np64(q), to_np64(k), to_np64(v), to_np64(do), scale,
+                                           causal, None if seqlens is None else seqlens.numpy(),
+                                           workers=8)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert_grad_parity(grad_errors(to_np64(got), ref), name)
+    if padded:  # keys past a batch element's length get exactly zero gradient
+        sl = seqlens.numpy()
+        for b in range(B):
+            assert (dk[b, sl[b]:] == 0).all() and (dv[b, sl[b]:] == 0).all()
+
+
+def test_backward_is_deterministic():
+    q, k, v = inputs.make_qkv(2, 700, 700, 8, 2, 128, 9100, q_mult=3.0)
+    do = inputs.make_dout(q.shape, 9101)
+    a = _fwd_bwd(q, k, v, do, 0.088, True, None)
+    b = _fwd_bwd(q, k, v, do, 0.088, True, None)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_full_size_slice():
+    """The benchmark's workload; one (batch, KV head) slice compared in full."""
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    x = inputs.workload_inputs(w)
+    do = inputs.make_dout(x["q"].shape, w.seed + 77)
+    print(f"[parity-bwd] full size {w.name}", flush=True)
+    dq, dk, dv = _fwd_bwd(x["q"], x["k"], x["v"], do, w.scale, w.causal, None)
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    G = w.Hq // w.Hkv
+    b, hkv = 1, 3
+    hs = slice(hkv * G, (hkv + 1) * G)
+    q = to_np64(x["q"][b:b + 1, :, hs])
+    k = to_np64(x["k"][b:b + 1, :, hkv:hkv + 1])
+    v = to_np64(x["v"][b:b + 1, :, hkv:hkv + 1])
+    rq, rk, rv = oracle.attention_backward(q, k, v, to_np64(do[b:b + 1, :, hs]), w.scale, w.causal,
+                                           workers=4)
+    for name, got, ref in (("dq", dq[b:b + 1, :, hs], rq), ("dk", dk[b:b + 1, :, hkv:hkv + 1], rk),
+                           ("dv", dv[b:b + 1, :, hkv:hkv + 1], rv)):
+        errs = grad_errors(to_np64(got), ref)
+        print(f"[parity-bwd] {w.name} {name}: {errs}", flush=True)
+        assert_grad_parity(errs, name)
