@@ -36,15 +36,24 @@ from exact_attention_18_amd import attn, inputs
 PEAK_BF16_TFLOPS = 2516.6
 METRIC = "attn fwd TFLOP/s bf16 hd128 causal N=8192 + % of MFMA bf16 peak"
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_18_amd", "csrc", "attn_fwd.hip")
+# Sources the forward kernels are built from (their hash keys the committed traffic figure).
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_18_amd", "csrc", n) for n in ("attn_fwd.hip", "cdna4.h")]
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 summary of this workload.
 
     The summary records FETCH_SIZE / WRITE_SIZE of the forward scaled by a
-    plain-copy calibration, and the sha256 of the kernel source it was taken
-    on; a summary of another kernel version gives None.
+    plain-copy calibration, and the sha256 of the forward's sources
+    (attn_fwd.hip, then cdna4.h) it was taken on; a summary of another
+    kernel version gives None.
     """
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}.md")
     if not os.path.exists(path):
@@ -54,7 +63,7 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith(("|", "-", "#", "`")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = kernel_source_sha256()
     if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
@@ -125,12 +134,63 @@ def cpu_baseline(w, x, target_s: float):
                       f"and P materialised, {workers} threads, {t_total:.1f} s wall"}
 
 
+def bench_backward(args, w, x, dev, fwd_flops):
+    """Times attn_bwd on the workload (FLOPs: 2.5x the forward, as the pages count them)."""
+    if w.varlen or w.d != 128:
+        print("the backward covers the batched d=128 workloads", file=sys.stderr)
+        sys.exit(2)
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
+    o, lse = attn.attn_fwd(q, k, v, w.scale, w.causal, sl)
+    do = inputs.make_dout(x["q"].shape, w.seed + 77).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((attn.load_library().attn_bwd_workspace_size(w.B, w.Hq, w.N),),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        attn.attn_bwd(q, k, v, o, lse, do, w.scale, w.causal, sl, workspace=ws, out=(dq, dk, dv))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(K):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    flops = 2.5 * fwd_flops
+    value = flops / (ms * 1e-3) / 1e12
+    # MFMA work actually issued: 5 contractions in the dK/dV kernel's four plus the
+    # dQ kernel's three (S and dP are formed in both), i.e. 3.5x the forward's two.
+    issued = 3.5 * fwd_flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "attn bwd TFLOP/s bf16 hd128 (2.5x forward FLOPs)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1) bf16; dO seeded likewise)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "algorithmic_flop": flops, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "mfma_issued_tflops": round(issued, 3)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--pass", dest="which", default="fwd", choices=("fwd", "bwd"),
+                    help="fwd (default): the forward; bwd: the backward (attn_bwd) of the same "
+                         "workload, from the forward's O and LSE and a seeded dO")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -160,8 +220,10 @@ def main():
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     x = inputs.workload_inputs(w)
     flops = algorithmic_flops(w, x)
-    step = make_step(w, x, dev)
     attn.load_library()
+    if args.which == "bwd":
+        return bench_backward(args, w, x, dev, flops)
+    step = make_step(w, x, dev)
 
     for _ in range(args.warmup):
         step()
