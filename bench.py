@@ -7,7 +7,8 @@ already resident in HBM.  W warm-up steps, then K timed steps on torch's
 current stream, bracketed by torch.cuda.synchronize().  Prints ONE JSON line.
 
 value       : algorithmic TFLOP/s of the step, FLOPs counted as the pages count
-              them: 4 * Nq * Nk * d per head, halved under the causal mask
+              them: 4 * Nq * Nk * d per head (2 * Nq * Nk * (d_qk + d_v) when the
+              score and value head dimensions differ), halved under the causal mask
               (FlashAttention-4 (papercache summary), experimental setup).
 roofline    : the forward kernel against the dense bf16 MFMA peak of MI355X
               (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU); its
@@ -72,18 +73,18 @@ def measured_traffic(workload: str):
 def algorithmic_flops(w: inputs.Workload, x) -> float:
     if w.varlen:
         lens = x["lengths"].to(torch.float64)
-        per = (4.0 * lens * lens * w.d).sum().item()
+        per = (2.0 * lens * lens * (w.d + w.d_v)).sum().item()
         f = per * w.Hq
     else:
         nk = (torch.full((w.B,), float(w.N), dtype=torch.float64) if x["seqlens_k"] is None
               else x["seqlens_k"].to(torch.float64))
-        f = (4.0 * w.N * nk * w.d).sum().item() * w.Hq
+        f = (2.0 * w.N * nk * (w.d + w.d_v)).sum().item() * w.Hq
     return f / 2.0 if w.causal else f
 
 
 def make_step(w, x, dev):
     q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape[:-1] + (w.d_v,), dtype=torch.bfloat16, device=dev)
     if w.varlen:
         cu = x["cu_seqlens_q"].to(dev)
         ms = x["max_seqlen"]
@@ -253,7 +254,7 @@ def main():
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, x, args.cpu_seconds)
-    cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+    cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "d_v": w.d_v,
            "causal": w.causal, "q_mult": w.q_mult, "algorithmic_flop": flops,
            "parallelism": "single GPU"}
     line = {

@@ -30,7 +30,7 @@ ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_varlen_plan", "attn_bwd", "attn_bwd_workspace_size",
+EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_varlen", "attn_varlen_plan", "attn_bwd", "attn_bwd_workspace_size",
            "attn_strerror", "attn_last_hip_error", "attn_version")
 
 _lib = None
@@ -48,6 +48,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_dims.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                  vp]
+    lib.attn_fwd_dims.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     i32, vp, vp]
     lib.attn_fwd_varlen.restype = i32
@@ -107,20 +110,22 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
              causal: bool = False, seqlens_k: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O, LSE = attention forward of bf16 q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d].
+    """O, LSE = attention forward of bf16 q [B,Nq,Hq,d], k [B,Nk,Hkv,d], v [B,Nk,Hkv,dv].
 
-    Returns O bf16 [B,Nq,Hq,d] and LSE fp32 [B,Hq,Nq] (natural log).  Launches
-    on torch's current stream of q's device and does not synchronise.
+    Returns O bf16 [B,Nq,Hq,dv] and LSE fp32 [B,Hq,Nq] (natural log).  dv == d,
+    or (d, dv) = (192, 128).  Launches on torch's current stream of q's device
+    and does not synchronise.
     """
     lib = load_library()
     _need(q, "q", torch.bfloat16)
     dev = q.device
     _need(k, "k", torch.bfloat16, dev)
     _need(v, "v", torch.bfloat16, dev)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError("expected q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d] of equal shape")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or v.shape[:3] != k.shape[:3]:
+        raise ValueError("expected q [B,Nq,Hq,d], k [B,Nk,Hkv,d] and v [B,Nk,Hkv,dv]")
     B, Nq, Hq, d = q.shape
     Bk, Nk, Hkv, dk = k.shape
+    dv = v.shape[3]
     if Bk != B or dk != d:
         raise ValueError("q and k disagree on batch or head dim")
     if scale is None:
@@ -130,19 +135,24 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
         if seqlens_k.shape != (B,):
             raise ValueError("seqlens_k must have shape [B]")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, Nq, Hq, dv), dtype=torch.bfloat16, device=dev)
     else:
         _need(out, "out", torch.bfloat16, dev)
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
+        if out.shape != (B, Nq, Hq, dv):
+            raise ValueError("out must have shape [B,Nq,Hq,dv]")
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
     else:
         _need(lse, "lse", torch.float32, dev)
         if lse.shape != (B, Hq, Nq):
             raise ValueError("lse must have shape [B,Hq,Nq]")
-    rc = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
-                      float(scale), int(bool(causal)), _ptr(seqlens_k), _stream_handle(dev))
+    if dv == d:
+        rc = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                          float(scale), int(bool(causal)), _ptr(seqlens_k), _stream_handle(dev))
+    else:
+        rc = lib.attn_fwd_dims(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk,
+                               d, dv, float(scale), int(bool(causal)), _ptr(seqlens_k),
+                               _stream_handle(dev))
     _check(rc, "attn_fwd")
     return out, lse
 

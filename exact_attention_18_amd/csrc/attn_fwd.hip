@@ -523,15 +523,21 @@ constexpr int kPpWaves = 8;
 constexpr int kPpThreads = 64 * kPpWaves;
 constexpr int kPpBr = kPpWaves * kRowsPerWave;  // 256 query rows per workgroup
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int DQK, int DV, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
-  using T = Tile<D>;
-  constexpr int CH = T::BC * D / 8 / (kPpThreads / 2);  // 16-byte chunks per thread per tile (one group moves a tile)
-  static_assert(CH >= 1 && CH * kPpThreads * 8 == 2 * T::BC * D, "tile split");
+  // Q and K rows have DQK elements, V and O rows DV (FlashAttention-4's (192, 128) shape).
+  using T = Tile<DQK>;   // key tiles, score slices
+  using TV = Tile<DV>;   // value tiles, output blocks
+  // 16-byte chunks per thread per tile (one group of 4 waves moves a tile)
+  constexpr int CHK = T::BC * DQK / 8 / (kPpThreads / 2);
+  constexpr int CHV = T::BC * DV / 8 / (kPpThreads / 2);
+  constexpr int CH = CHK > CHV ? CHK : CHV;
+  static_assert(CHK * kPpThreads * 8 == 2 * T::BC * DQK && CHV * kPpThreads * 8 == 2 * T::BC * DV,
+                "tile split");
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[T::K_ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[T::K_ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[T::V_ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[T::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[TV::V_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[TV::V_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -573,11 +579,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const int q0 = qb * kPpBr;
   if (q0 >= q_len) return;  // uniform over the workgroup, before any barrier
 
-  const long q_stride = (long)p.Hq * D;
-  const long kv_stride = (long)p.Hkv * D;
-  const __bf16* qbase = p.q + q_row0 * q_stride + (long)h * D;
-  const __bf16* kbase = p.k + k_row0 * kv_stride + (long)hkv * D;
-  const __bf16* vbase = p.v + k_row0 * kv_stride + (long)hkv * D;
+  const long q_stride = (long)p.Hq * DQK;
+  const long o_stride = (long)p.Hq * DV;
+  const long k_stride = (long)p.Hkv * DQK;
+  const long v_stride = (long)p.Hkv * DV;
+  const __bf16* qbase = p.q + q_row0 * q_stride + (long)h * DQK;
+  const __bf16* kbase = p.k + k_row0 * k_stride + (long)hkv * DQK;
+  const __bf16* vbase = p.v + k_row0 * v_stride + (long)hkv * DV;
 
   const int wrow0 = q0 + chunk * kRowsPerWave;
   const int qrow = wrow0 + l32;
@@ -593,15 +601,14 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   if (CAUSAL) kv_end = min(nk, min(q0 + kPpBr, q_len));
   const int n_tiles = (kv_end + T::BC - 1) / T::BC;
 
-  const uint32_t row_bytes = static_cast<uint32_t>(kv_stride) * 2u;
   auto k_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
-    const int rem16 = c % (16 * (D / 8));
-    *row = 16 * (c / (16 * (D / 8))) + rem16 % 16;
+    const int rem16 = c % (16 * (DQK / 8));
+    *row = 16 * (c / (16 * (DQK / 8))) + rem16 % 16;
     *colb = (rem16 / 16) * 16;
   };
   auto v_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
-    const int w = c % (D / 2);
-    *row = 4 * (c / (D / 2)) + (w % 8) / 2;
+    const int w = c % (DV / 2);
+    *row = 4 * (c / (DV / 2)) + (w % 8) / 2;
     *colb = (16 * (w / 8) + 8 * (w % 2)) * 2;
   };
   // Group 0 moves V tiles, group 1 K tiles; wave w of a group fills the
@@ -609,6 +616,8 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   // Rows past kv_end read as zero (buffer range check) and are masked.
   const int gw = wave & 3;
   const bool fetch_v = grp == 0;
+  const int nch = fetch_v ? CHV : CHK;  // chunks per lane of this group's tiles
+  const uint32_t row_bytes = static_cast<uint32_t>(fetch_v ? v_stride : k_stride) * 2u;
   uint32_t goff[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -623,10 +632,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     const int kv0 = t * T::BC;
     const int nrows = min(kv_end - kv0, T::BC);
     const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(gbase + kv0 * kv_stride), (short)0, nrows * (int)row_bytes, kBufferFlags);
+        const_cast<__bf16*>(gbase + (long)kv0 * (row_bytes / 2)), (short)0, nrows * (int)row_bytes,
+        kBufferFlags);
 #pragma unroll
     for (int i = 0; i < CH; ++i)
-      stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, goff[i], 0, 0));
+      if (i < nch)
+        stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, goff[i], 0, 0));
   };
   auto store_chunk = [&](__bf16* dst, auto C) __attribute__((always_inline)) {
     constexpr int i = decltype(C)::value;
@@ -635,11 +646,11 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   auto store_tile = [&](__bf16* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CH; ++i)
-      *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
+      if (i < nch) *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
   };
 
-  const int k_lane = ((l32 >> 4) * (D / 8) + g) * 128 + (l32 & 15) * 8;
-  const int v_lane = g * T::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
+  const int k_lane = ((l32 >> 4) * (DQK / 8) + g) * 128 + (l32 & 15) * 8;
+  const int v_lane = g * TV::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
 
   const float c = p.c;
   // Tiles crossing the key tail or the diagonal (or lying wholly above this
@@ -651,9 +662,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
   f32x16 sv[T::KT];
   u32x4 pv_op[T::KT][2];
-  f32x16 acc[T::DT];
+  f32x16 acc[TV::DT];
 #pragma unroll
-  for (int dt = 0; dt < T::DT; ++dt) acc[dt] = f32x16{};
+  for (int dt = 0; dt < TV::DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
   float m_run = -INFINITY;
@@ -661,10 +672,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
   // ---- MFMA phase: S_j = K_j Q^T (key blocks interleaved), then O += P_{j-1} V_{j-1}.
   constexpr int kS = T::KT * T::KS;
-  constexpr int kPv = T::KT * 2 * T::DT;
+  constexpr int kPv = T::KT * 2 * TV::DT;
   constexpr int kAhead = 3;       // LDS operand reads run this many MFMAs ahead
   constexpr int kMoveFirst = 4;   // tile-store slots inside the MFMA phase
-  constexpr int kMoveStride = 8;
+  // 8 slices apart where that fits, else spread evenly over the phase
+  constexpr int kMoveStride =
+      kMoveFirst + (CH - 1) * 8 < kS + kPv ? 8 : (kS + kPv - kMoveFirst) / CH;
   static_assert(kMoveFirst + (CH - 1) * kMoveStride < kS + kPv, "move slots");
   // mid(c) runs after slice kMoveFirst + c*kMoveStride (tile chunk c moves to LDS there).
   auto mphase = [&](const __bf16* kb, const __bf16* vb, auto&& mid) __attribute__((always_inline)) {
@@ -674,12 +687,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       constexpr int i = decltype(I)::value;
       if constexpr (i < n0) {
         constexpr int kt = i % T::KT, ks = i / T::KT;
-        return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (D / 8) + 2 * ks) * 128);
+        return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (DQK / 8) + 2 * ks) * 128);
       } else {
         constexpr int s = i - n0;
-        constexpr int kt = s / (2 * T::DT), hh = (s / T::DT) % 2, dt = s % T::DT;
-        const __bf16* p0 = vb + v_lane + (8 * kt + 4 * hh) * T::QUAD + dt * 128;
-        return read_tr_pair(p0, p0 + 2 * T::QUAD);
+        constexpr int kt = s / (2 * TV::DT), hh = (s / TV::DT) % 2, dt = s % TV::DT;
+        const __bf16* p0 = vb + v_lane + (8 * kt + 4 * hh) * TV::QUAD + dt * 128;
+        return read_tr_pair(p0, p0 + 2 * TV::QUAD);
       }
     };
     bf16x8 opnd[kAhead];
@@ -695,7 +708,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
       } else {
         constexpr int s = i - n0;
-        constexpr int kt = s / (2 * T::DT), hh = (s / T::DT) % 2, dt = s % T::DT;
+        constexpr int kt = s / (2 * TV::DT), hh = (s / TV::DT) % 2, dt = s % TV::DT;
         acc[dt] = mfma32(a, __builtin_bit_cast(bf16x8, pv_op[kt][hh]), acc[dt]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -748,7 +761,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     l_run = l_run * alpha + (ls0 + ls1);
     if (any) {
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
     }
   };
 
@@ -783,7 +796,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     auto move = [&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
       if (st < n_tiles) {
-        store_chunk(dst, C);
+        if (c < nch) store_chunk(dst, C);
         if constexpr (c == CH - 1) {
           if (st + 1 < n_tiles) load_tile(st + 1);
         }
@@ -798,7 +811,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
 #pragma unroll
   for (int kt = 0; kt < T::KT; ++kt) pv_op[kt][0] = pv_op[kt][1] = u32x4{};
-  for (int i = tid; i < T::V_ELEMS / 8; i += kPpThreads)
+  for (int i = tid; i < TV::V_ELEMS / 8; i += kPpThreads)
     reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
   // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
   if (fetch_v) {
@@ -821,9 +834,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const float l_tot = pair_sum(l_run);
   if (qrow < q_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = p.o + (q_row0 + qrow) * q_stride + (long)h * D;
+    __bf16* orow = p.o + (q_row0 + qrow) * o_stride + (long)h * DV;
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt)
+    for (int dt = 0; dt < TV::DT; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         bf16x4 ov;
@@ -892,7 +905,7 @@ template <int D, bool CAUSAL, bool VARLEN>
 int launch_one(const Params& p, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   if constexpr (use_pp(D))
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kPpThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, D, CAUSAL, VARLEN>), dim3(grid), dim3(kPpThreads), 0,
                        stream, p);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream,
@@ -972,6 +985,52 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   return dispatch(p, d, causal != 0, false, static_cast<int>(grid),
                   static_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_fwd_dims(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Nq, int Nk, int d_qk, int d_v, float scale,
+                             int causal, const int32_t* seqlens_k, void* stream) {
+  if (d_qk == d_v)
+    return attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d_qk, scale, causal, seqlens_k, stream);
+  if (B < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SIZE;
+  int rc = check_common(Hq, Hkv, 128, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!(d_qk == 192 && d_v == 128)) return ATTN_ERR_HEAD_DIM;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  rc = check_buffers(q, k, v, o, lse, Nk > 0);
+  if (rc != ATTN_OK) return rc;
+  const long nqb = (Nq + kPpBr - 1) / kPpBr;
+  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv));
+  if (grid > INT_MAX || (long)B * Nq > INT_MAX || (long)B * Nk > INT_MAX) return ATTN_ERR_TOO_LARGE;
+  Params p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<__bf16*>(o);
+  p.lse = lse;
+  p.seqlens_k = seqlens_k;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.nqb = static_cast<int>(nqb);
+  p.num_seqs = B;
+  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, true, false>), dim3((unsigned)grid),
+                       dim3(kPpThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, false, false>), dim3((unsigned)grid),
+                       dim3(kPpThreads), 0, st, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    attn_detail::last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
 }
 
 extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

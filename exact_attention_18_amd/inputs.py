@@ -50,6 +50,11 @@ class Workload:
     varlen_seqs: int = 0
     varlen_lo: int = 0
     varlen_hi: int = 0
+    dv: int = 0  # value / output head dimension when it differs from d
+
+    @property
+    def d_v(self) -> int:
+        return self.dv or self.d
 
     @property
     def scale(self) -> float:
@@ -79,17 +84,21 @@ WORKLOADS = {
     "varlen_causal_8seq_h32_d128": Workload("varlen_causal_8seq_h32_d128", 1, 32, 32, 16384, 128,
                                             True, 5001, varlen_seed=5002, varlen_seqs=8,
                                             varlen_lo=2048, varlen_hi=16384),
+    # Asymmetric head dimensions: scores at d = 192, values at d = 128, 16 heads,
+    # batch 4 x 8192 tokens (the (192, 128) shape of the FlashAttention-4 sweep).
+    "asym_causal_b4_h16_n8192_dqk192_dv128": Workload("asym_causal_b4_h16_n8192_dqk192_dv128", 4,
+                                                      16, 16, 8192, 192, True, 6001, dv=128),
 }
 
 HEADLINE = "gqa_causal_b4_hq32_hkv8_n8192_d128"
 
 
-def make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=1.0):
-    """Q [B,Nq,Hq,d], K [B,Nk,Hkv,d], V [B,Nk,Hkv,d] as bf16 CPU tensors."""
+def make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=1.0, d_v=None):
+    """Q [B,Nq,Hq,d], K [B,Nk,Hkv,d], V [B,Nk,Hkv,d_v] (d_v defaults to d) as bf16 CPU tensors."""
     g = torch.Generator().manual_seed(int(seed))
     q = torch.randn((B, Nq, Hq, d), generator=g, dtype=torch.float32)
     k = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)
-    v = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Nk, Hkv, d if d_v is None else d_v), generator=g, dtype=torch.float32)
     if q_mult != 1.0:
         q.mul_(q_mult)
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
@@ -139,7 +148,7 @@ def workload_inputs(w: Workload):
         q, k, v = make_packed_qkv(total, total, w.Hq, w.Hkv, w.d, w.seed, w.q_mult)
         return dict(q=q, k=k, v=v, cu_seqlens_q=cu, cu_seqlens_k=cu.clone(), lengths=lengths,
                     max_seqlen=int(lengths.max()))
-    q, k, v = make_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.d, w.seed, w.q_mult)
+    q, k, v = make_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.d, w.seed, w.q_mult, d_v=w.d_v)
     seqlens = None
     if w.pad_seed is not None:
         seqlens = make_seqlens(w.B, w.pad_lo, w.N, w.pad_seed)

@@ -95,6 +95,19 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              void* stream);
 
 /*
+ * Batched forward with different head dimensions for the scores and the
+ * values: q, k are bf16 [.., d_qk], v and o bf16 [.., d_v]; everything else
+ * (masks, GQA, seqlens_k, lse, errors) as for attn_fwd.  Supported pairs:
+ * d_qk == d_v (then this is attn_fwd), and (d_qk, d_v) = (192, 128), the
+ * asymmetric shape of the FlashAttention-4 benchmarks ("FlashAttention-4"
+ * (papercache summary), experimental setup: head dimensions 64, 128 and
+ * (192, 128)).  Other pairs return ATTN_ERR_HEAD_DIM.
+ */
+int attn_fwd_dims(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                  int Hkv, int Nq, int Nk, int d_qk, int d_v, float scale, int causal,
+                  const int32_t* seqlens_k, void* stream);
+
+/*
  * Packed variable-length forward: num_seqs sequences stored back to back.
  * Sequence z owns query rows cu_seqlens_q[z] .. cu_seqlens_q[z+1]-1 and keys
  * cu_seqlens_k[z] .. cu_seqlens_k[z+1]-1; indices are local to the sequence

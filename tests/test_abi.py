@@ -204,3 +204,33 @@ def test_attn_bwd_workspace_size():
     assert lib.attn_bwd_workspace_size(2, 4, 100) == 2 * 4 * 2 * 4 * 100
     assert lib.attn_bwd_workspace_size(0, 4, 100) == 0
     assert lib.attn_bwd_workspace_size(3, -1, 100) == 0
+
+
+def _dims(d_qk, d_v, **kw):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4, Hkv=2, Nq=256, Nk=256, scale=0.07,
+             causal=1)
+    a.update(kw)
+    return lib.attn_fwd_dims(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]), a["B"],
+                             a["Hq"], a["Hkv"], a["Nq"], a["Nk"], d_qk, d_v, a["scale"], a["causal"],
+                             None, None)
+
+
+@pytest.mark.parametrize("d_qk,d_v,kw,code", [
+    (192, 64, {}, attn.ATTN_ERR_HEAD_DIM),
+    (256, 128, {}, attn.ATTN_ERR_HEAD_DIM),
+    (128, 64, {}, attn.ATTN_ERR_HEAD_DIM),
+    (96, 96, {}, attn.ATTN_ERR_HEAD_DIM),
+    (192, 128, dict(q=None), attn.ATTN_ERR_NULL),
+    (192, 128, dict(o=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (192, 128, dict(Hq=3, Hkv=2), attn.ATTN_ERR_HEADS),
+    (192, 128, dict(Nk=-1), attn.ATTN_ERR_SIZE),
+    (192, 128, dict(scale=-1.0), attn.ATTN_ERR_SIZE),
+])
+def test_attn_fwd_dims_rejects_bad_arguments(d_qk, d_v, kw, code):
+    assert _dims(d_qk, d_v, **kw) == code
+
+
+def test_attn_fwd_dims_empty_is_a_noop():
+    assert _dims(192, 128, B=0, q=None, k=None, v=None, o=None, lse=None) == attn.ATTN_OK

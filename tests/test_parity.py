@@ -76,6 +76,34 @@ def test_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, d, causal, padded):
         assert (o_np[empty] == 0).all()
 
 
+ASYM = [
+    # B, Nq, Nk, Hq, Hkv, causal, padded  (d_qk = 192, d_v = 128)
+    (1, 300, 300, 4, 4, True, False),
+    (2, 130, 517, 2, 1, False, False),
+    (3, 257, 257, 4, 2, True, True),
+    (1, 1, 1, 1, 1, False, False),
+    (1, 64, 0, 2, 1, True, False),
+]
+
+
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal,padded", ASYM)
+def test_asymmetric_head_dims_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded):
+    seed = 7500 + B * 31 + Nq * 7 + Nk + Hq * 3 + int(causal)
+    q, k, v = inputs.make_qkv(B, Nq, Nk, Hq, Hkv, 192, seed, q_mult=2.0, d_v=128)
+    seqlens = None
+    if padded:
+        seqlens = inputs.make_seqlens(B, 0, Nk, seed + 1)
+        seqlens[0] = 0
+    scale = 1.0 / math.sqrt(192)
+    print(f"[parity] (192,128) B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
+    o, lse = _run(q, k, v, scale, causal, seqlens)
+    assert o.shape == (B, Nq, Hq, 128)
+    o_ref, lse_ref = oracle.attention_forward(to_np64(q), to_np64(k), to_np64(v), scale, causal,
+                                              None if seqlens is None else seqlens.numpy(),
+                                              workers=8)
+    assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "(192,128)")
+
+
 def test_varlen_small_full_oracle():
     lengths = torch.tensor([1, 130, 257, 0, 64, 200], dtype=torch.int32)
     cu = inputs.cu_from_lengths(lengths)
