@@ -18,6 +18,8 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_varlen,
     attention_rows,
+    attention_forward_blocksparse,
+    block_mask_to_elements,
     online_softmax_head,
 )
 from .backward import (  # noqa: F401,E402

@@ -49,6 +49,8 @@ __all__ = [
     "attention_forward_varlen",
     "attention_rows",
     "online_softmax_head",
+    "block_mask_to_elements",
+    "attention_forward_blocksparse",
 ]
 
 
@@ -66,7 +68,7 @@ def _visible(rows, nk, causal, nk_valid):
     return vis
 
 
-def attention_probs(q, k, scale, causal=False, nk_valid=None, rows=None):
+def attention_probs(q, k, scale, causal=False, nk_valid=None, rows=None, allowed=None):
     """Materialised scores, probabilities and LSE for one head.
 
     q: [Nq, d], k: [Nk, d].  Returns (S, P, LSE) for the requested query rows
@@ -84,6 +86,8 @@ def attention_probs(q, k, scale, causal=False, nk_valid=None, rows=None):
     rows = np.arange(nq) if rows is None else np.asarray(rows)
     s = scale * (q[rows] @ k.T)
     vis = _visible(rows, nk, causal, nk_valid)
+    if allowed is not None:  # extra visibility mask [Nq, Nk] (block-sparse)
+        vis = vis & np.asarray(allowed, dtype=bool)[rows]
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1) if nk > 0 else np.full(rows.shape[0], -np.inf)
     has_key = np.isfinite(m)
@@ -96,7 +100,8 @@ def attention_probs(q, k, scale, causal=False, nk_valid=None, rows=None):
     return s, p, lse
 
 
-def attention_head(q, k, v, scale, causal=False, nk_valid=None, rows=None, chunk=256):
+def attention_head(q, k, v, scale, causal=False, nk_valid=None, rows=None, chunk=256,
+                   allowed=None):
     """O = P V and LSE for one head, P materialised a chunk of rows at a time.
 
     q: [Nq, d], k: [Nk, d], v: [Nk, dv].  Returns (O [R, dv], LSE [R]) for the
@@ -112,7 +117,7 @@ def attention_head(q, k, v, scale, causal=False, nk_valid=None, rows=None, chunk
     lse = np.zeros(rows.shape[0])
     for r0 in range(0, rows.shape[0], chunk):
         rr = rows[r0 : r0 + chunk]
-        _, p, l_ = attention_probs(q, k, scale, causal, nk_valid, rows=rr)
+        _, p, l_ = attention_probs(q, k, scale, causal, nk_valid, rows=rr, allowed=allowed)
         out[r0 : r0 + rr.shape[0]] = p @ v
         lse[r0 : r0 + rr.shape[0]] = l_
     return out, lse
@@ -220,6 +225,44 @@ def attention_rows(q, k, v, scale, causal, samples, seqlens_k=None):
                                 scale, causal, nk_valid, rows=[i])
         out[n] = o_[0]
         lse[n] = l_[0]
+    return out, lse
+
+
+def block_mask_to_elements(block_mask, nq, nk, bq, bk):
+    """Element visibility [nq, nk] of a block mask: (i, j) allowed iff block_mask[i//bq, j//bk]."""
+    bm = np.asarray(block_mask, dtype=bool)
+    return bm[np.arange(nq)[:, None] // bq, np.arange(nk)[None, :] // bk]
+
+
+def attention_forward_blocksparse(q, k, v, scale, block_mask, bq=128, bk=128, causal=False,
+                                  seqlens_k=None, workers=None):
+    """Block-sparse forward: S masked to -inf outside the nonzero blocks, then softmax, P V.
+
+    The operator of block-sparse FlashAttention (FlashAttention notes
+    (xwysyy), "Block-Sparse FlashAttention": P = softmax(S with the positions
+    of zero blocks of the block mask set to -inf), O = P V), on top of the
+    causal / padding masks.  block_mask: [Hm, ceil(Nq/bq), ceil(Nk/bk)] with
+    Hm = 1 (shared by every head) or Hq; shared by the batch.  Layouts as in
+    attention_forward.  Returns O [B, Nq, Hq, dv] and LSE [B, Hq, Nq].
+    """
+    B, Nq, Hq, _ = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    bm = np.asarray(block_mask)
+    out = np.zeros((B, Nq, Hq, v.shape[3]))
+    lse = np.zeros((B, Hq, Nq))
+    allowed = [block_mask_to_elements(bm[h], Nq, Nk, bq, bk) for h in range(bm.shape[0])]
+    jobs = [(b, h) for b in range(B) for h in range(Hq)]
+
+    def one(bh):
+        b, h = bh
+        nk_valid = None if seqlens_k is None else int(seqlens_k[b])
+        return attention_head(q[b, :, h], k[b, :, h // G], v[b, :, h // G], scale, causal, nk_valid,
+                              allowed=allowed[h if len(allowed) > 1 else 0])
+
+    for (b, h), (o_bh, l_bh) in zip(jobs, _run_jobs(one, jobs, workers)):
+        out[b, :, h] = o_bh
+        lse[b, h] = l_bh
     return out, lse
 
 
