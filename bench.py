@@ -75,6 +75,12 @@ def algorithmic_flops(w: inputs.Workload, x) -> float:
         lens = x["lengths"].to(torch.float64)
         per = (2.0 * lens * lens * (w.d + w.d_v)).sum().item()
         f = per * w.Hq
+    elif w.sparse:  # the (row, key) pairs inside nonzero blocks, within N x N
+        bm = x["block_mask"][0].to(torch.float64)
+        sizes = torch.full((bm.shape[0],), float(inputs.SPARSE_BLOCK), dtype=torch.float64)
+        sizes[-1] = w.N - inputs.SPARSE_BLOCK * (bm.shape[0] - 1)
+        pairs = (sizes[:, None] * bm * sizes[None, :]).sum().item()
+        f = 2.0 * pairs * (w.d + w.d_v) * w.B * w.Hq
     else:
         nk = (torch.full((w.B,), float(w.N), dtype=torch.float64) if x["seqlens_k"] is None
               else x["seqlens_k"].to(torch.float64))
@@ -96,6 +102,12 @@ def make_step(w, x, dev):
             attn.attn_varlen_plan(cu, cu, ms, ms, w.causal, out=plan)
             attn.attn_fwd_varlen(q, k, v, cu, cu, ms, ms, w.scale, w.causal, out=out, lse=lse,
                                  seq_order=plan)
+    elif w.sparse:
+        bm = x["block_mask"].to(dev)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            attn.attn_fwd_blocksparse(q, k, v, bm, w.scale, w.causal, out=out, lse=lse)
     else:
         sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
@@ -111,7 +123,7 @@ def cpu_baseline(w, x, target_s: float):
     from oracle.attention import default_workers
 
     workers = default_workers()
-    if w.varlen:
+    if w.varlen or w.sparse:
         return None
     q = x["q"].float().numpy()
     k = x["k"].float().numpy()
@@ -137,8 +149,8 @@ def cpu_baseline(w, x, target_s: float):
 
 def bench_backward(args, w, x, dev, fwd_flops):
     """Times attn_bwd on the workload (FLOPs: 2.5x the forward, as the pages count them)."""
-    if w.varlen or w.d != 128:
-        print("the backward covers the batched d=128 workloads", file=sys.stderr)
+    if w.varlen or w.sparse or w.d != 128 or w.d_v != 128:
+        print("the backward covers the batched dense d=128 workloads", file=sys.stderr)
         sys.exit(2)
     q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
     sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)

@@ -30,7 +30,7 @@ ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
 
-EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_varlen", "attn_varlen_plan", "attn_bwd", "attn_bwd_workspace_size",
+EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen", "attn_varlen_plan", "attn_bwd", "attn_bwd_workspace_size",
            "attn_strerror", "attn_last_hip_error", "attn_version")
 
 _lib = None
@@ -51,6 +51,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_dims.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                                   vp]
     lib.attn_fwd_dims.restype = i32
+    lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                         vp, vp, i32, vp]
+    lib.attn_fwd_blocksparse.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     i32, vp, vp]
     lib.attn_fwd_varlen.restype = i32
@@ -285,3 +288,40 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                       int(bool(causal)), _ptr(seqlens_k), _stream_handle(dev))
     _check(rc, "attn_bwd")
     return dq, dk, dv
+
+
+SPARSE_BLOCK = 128  # block-sparse mask granularity (query rows and keys)
+
+
+def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
+                         scale: Optional[float] = None, causal: bool = False,
+                         seqlens_k: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-sparse forward; block_mask uint8 [1 or Hq, ceil(Nq/128), ceil(Nk/128)] on the GPU."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    _need(block_mask, "block_mask", torch.uint8, dev)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d] of equal shape")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    nbq, nbk = -(-Nq // SPARSE_BLOCK), -(-Nk // SPARSE_BLOCK)
+    if block_mask.dim() != 3 or block_mask.shape[1:] != (nbq, nbk):
+        raise ValueError(f"block_mask must have shape [1 or Hq, {nbq}, {nbk}]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if seqlens_k is not None:
+        _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    rc = lib.attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq,
+                                  Nk, d, float(scale), int(bool(causal)), _ptr(seqlens_k),
+                                  _ptr(block_mask), int(block_mask.shape[0]), _stream_handle(dev))
+    _check(rc, "attn_fwd_blocksparse")
+    return out, lse

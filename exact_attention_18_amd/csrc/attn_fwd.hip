@@ -120,7 +120,12 @@ struct Params {
   int nqb;     // query blocks per (sequence, head)
   int num_seqs;
   float c;  // scale * log2(e)
+  const uint8_t* block_mask;  // block-sparse form: [mask_heads, nbq, nbk] of 128 x 128 blocks
+  int mask_heads, nbq, nbk;
 };
+
+constexpr int kSparseBlock = 128;      // block-sparse mask granularity (rows and keys)
+constexpr int kMaxSparseTiles = 4096;  // key tiles a block-sparse launch may visit (Nk <= 262144)
 
 // Work decode.  A unit is one (batch element or sequence, KV head) pair,
 // u = b * Hkv + hkv.  Units are dealt round-robin to the 8 XCDs (the hardware
@@ -523,7 +528,7 @@ constexpr int kPpWaves = 8;
 constexpr int kPpThreads = 64 * kPpWaves;
 constexpr int kPpBr = kPpWaves * kRowsPerWave;  // 256 query rows per workgroup
 
-template <int DQK, int DV, bool CAUSAL, bool VARLEN>
+template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool SPARSE = false>
 __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   // Q and K rows have DQK elements, V and O rows DV (FlashAttention-4's (192, 128) shape).
   using T = Tile<DQK>;   // key tiles, score slices
@@ -601,6 +606,41 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   if (CAUSAL) kv_end = min(nk, min(q0 + kPpBr, q_len));
   const int n_tiles = (kv_end + T::BC - 1) / T::BC;
 
+  // Block-sparse: the key tiles whose 128-key block is set in either of this
+  // workgroup's two 128-row mask rows, compacted in order into an LDS list
+  // (FlashAttention notes (xwysyy), "Block-Sparse FlashAttention": zero
+  // blocks are skipped).  Dense launches visit tiles 0 .. n_tiles-1.
+  __shared__ int tile_list[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int wave_count[SPARSE ? kPpWaves : 1];
+  int n_iter = n_tiles;
+  const uint8_t* mrow = nullptr;  // this wave's mask row
+  if constexpr (SPARSE) {
+    const int hm = p.mask_heads == 1 ? 0 : h;
+    const uint8_t* mask0 = p.block_mask + ((long)hm * p.nbq + q0 / kSparseBlock) * p.nbk;
+    const bool two_rows = q0 / kSparseBlock + 1 < p.nbq;
+    // (waves whose rows lie past Nq read the last mask row; their rows are not stored)
+    mrow = p.block_mask + ((long)hm * p.nbq + min(wrow0 / kSparseBlock, p.nbq - 1)) * p.nbk;
+    n_iter = 0;
+    for (int c0 = 0; c0 < n_tiles; c0 += kPpThreads) {
+      const int j = c0 + tid;
+      const int mc = j * T::BC / kSparseBlock;
+      const bool vis = j < n_tiles && (mask0[mc] != 0 || (two_rows && mask0[p.nbk + mc] != 0));
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
+      if (lane == 0) wave_count[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int before = n_iter;
+      for (int w = 0; w < wave; ++w) before += wave_count[w];
+      const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      if (vis) tile_list[before + rank] = j;
+      for (int w = 0; w < kPpWaves; ++w) n_iter += wave_count[w];
+      __syncthreads();
+    }
+  }
+  // Key tile visited at list position t.
+  auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return tile_list[t]; else return t;
+  };
+
   auto k_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
     const int rem16 = c % (16 * (DQK / 8));
     *row = 16 * (c / (16 * (DQK / 8))) + rem16 % 16;
@@ -629,7 +669,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const __bf16* gbase = fetch_v ? vbase : kbase;
   u32x4 stage[CH];
   auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const int kv0 = t * T::BC;
+    const int kv0 = tile_of(t) * T::BC;
     const int nrows = min(kv_end - kv0, T::BC);
     const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16*>(gbase + (long)kv0 * (row_bytes / 2)), (short)0, nrows * (int)row_bytes,
@@ -655,9 +695,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const float c = p.c;
   // Tiles crossing the key tail or the diagonal (or lying wholly above this
   // wave's rows, which the mask then empties) are masked.
+  // This wave's rows see the tile's 128-key block (block-sparse; else always).
+  auto block_visible = [&](int tile) __attribute__((always_inline)) -> bool {
+    if constexpr (SPARSE) return mrow[tile * T::BC / kSparseBlock] != 0; else return true;
+  };
   auto needs_mask = [&](int tile) __attribute__((always_inline)) {
     const int kv0 = tile * T::BC;
-    return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0);
+    return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0) || !block_visible(tile);
   };
 
   f32x16 sv[T::KT];
@@ -721,18 +765,20 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   };
   auto apply_mask = [&](int tile) __attribute__((always_inline)) {
     const int kv0 = tile * T::BC;
+    const bool bvis = block_visible(tile);
 #pragma unroll
     for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool vis = key < nk && (!CAUSAL || key <= qrow);
+        const bool vis = bvis && key < nk && (!CAUSAL || key <= qrow);
         if (!vis) sv[kt][r] = -INFINITY;
       }
   };
   // ---- VALU phase: online softmax of S_j -> P_j, O rescale when the max moved.
   auto vphase = [&](int j) __attribute__((always_inline)) {
-    if (needs_mask(j)) apply_mask(j);
+    const int tile = tile_of(j);
+    if (needs_mask(tile)) apply_mask(tile);
     float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 32; e += 4) {
@@ -785,7 +831,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   };
   // One period: M_j (+ tile store and load), barrier, V_j, barrier.  At j = 0
   // the P V adds zero (P and the V buffer it reads are zeroed first); at
-  // j = n_tiles the scores come from a stale K tile and are never used.
+  // j = n_iter the scores come from a stale K tile and are never used.
   auto period = [&](int j, auto J) __attribute__((always_inline)) {
     constexpr int j2 = decltype(J)::value;  // j % 2
     const int st = fetch_v ? j : j + 1;  // tile stored in this phase
@@ -795,17 +841,17 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     // into the freed registers.
     auto move = [&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
-      if (st < n_tiles) {
+      if (st < n_iter) {
         if (c < nch) store_chunk(dst, C);
         if constexpr (c == CH - 1) {
-          if (st + 1 < n_tiles) load_tile(st + 1);
+          if (st + 1 < n_iter) load_tile(st + 1);
         }
       }
     };
     mphase(kbuf(std::integral_constant<int, j2>{}), vbuf(std::integral_constant<int, j2 + 1>{}), move);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this phase's LDS stores are done
     barrier();
-    if (j < n_tiles) vphase(j);
+    if (j < n_iter) vphase(j);
     barrier();
   };
 
@@ -815,20 +861,20 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
   // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
   if (fetch_v) {
-    if (n_tiles > 0) load_tile(0);
+    if (n_iter > 0) load_tile(0);
   } else {
-    if (n_tiles > 0) { load_tile(0); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
-    if (n_tiles > 1) load_tile(1);
+    if (n_iter > 0) { load_tile(0); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
+    if (n_iter > 1) load_tile(1);
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   barrier();
   if (grp == 1) barrier();  // group 1 starts half a period late
   int j = 0;
-  for (; j + 1 <= n_tiles; j += 2) {
+  for (; j + 1 <= n_iter; j += 2) {
     period(j, std::integral_constant<int, 0>{});
     period(j + 1, std::integral_constant<int, 1>{});
   }
-  if (j <= n_tiles) period(j, std::integral_constant<int, 0>{});
+  if (j <= n_iter) period(j, std::integral_constant<int, 0>{});
   if (grp == 0) barrier();
 
   const float l_tot = pair_sum(l_run);
@@ -1024,6 +1070,58 @@ extern "C" int attn_fwd_dims(const void* q, const void* k, const void* v, void* 
                        dim3(kPpThreads), 0, st, p);
   else
     hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, false, false>), dim3((unsigned)grid),
+                       dim3(kPpThreads), 0, st, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    attn_detail::last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                    float scale, int causal, const int32_t* seqlens_k,
+                                    const uint8_t* block_mask, int mask_heads, void* stream) {
+  if (B < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SIZE;
+  int rc = check_common(Hq, Hkv, d, scale);
+  if (rc != ATTN_OK) return rc;
+  if (d != 128) return ATTN_ERR_HEAD_DIM;
+  if (mask_heads != 1 && mask_heads != Hq) return ATTN_ERR_HEADS;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (block_mask == nullptr) return ATTN_ERR_NULL;
+  rc = check_buffers(q, k, v, o, lse, Nk > 0);
+  if (rc != ATTN_OK) return rc;
+  if ((long)Nk > (long)kMaxSparseTiles * 64) return ATTN_ERR_TOO_LARGE;
+  const long nqb = (Nq + kPpBr - 1) / kPpBr;
+  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv));
+  if (grid > INT_MAX || (long)B * Nq > INT_MAX || (long)B * Nk > INT_MAX) return ATTN_ERR_TOO_LARGE;
+  Params p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<__bf16*>(o);
+  p.lse = lse;
+  p.seqlens_k = seqlens_k;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.nqb = static_cast<int>(nqb);
+  p.num_seqs = B;
+  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.block_mask = block_mask;
+  p.mask_heads = mask_heads;
+  p.nbq = (Nq + kSparseBlock - 1) / kSparseBlock;
+  p.nbk = (Nk + kSparseBlock - 1) / kSparseBlock;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, true, false, true>), dim3((unsigned)grid),
+                       dim3(kPpThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, false, false, true>), dim3((unsigned)grid),
                        dim3(kPpThreads), 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -51,6 +51,8 @@ class Workload:
     varlen_lo: int = 0
     varlen_hi: int = 0
     dv: int = 0  # value / output head dimension when it differs from d
+    sparse_window: int = -1  # block-sparse: key blocks within this distance of the query block ...
+    sparse_global: int = 0   # ... plus the first sparse_global key blocks (128 x 128 blocks)
 
     @property
     def d_v(self) -> int:
@@ -59,6 +61,10 @@ class Workload:
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
+
+    @property
+    def sparse(self) -> bool:
+        return self.sparse_window >= 0
 
     @property
     def varlen(self) -> bool:
@@ -88,7 +94,21 @@ WORKLOADS = {
     # batch 4 x 8192 tokens (the (192, 128) shape of the FlashAttention-4 sweep).
     "asym_causal_b4_h16_n8192_dqk192_dv128": Workload("asym_causal_b4_h16_n8192_dqk192_dv128", 4,
                                                       16, 16, 8192, 192, True, 6001, dv=128),
+    # Block-sparse: sliding window of +-8 blocks of 128 plus one global key block,
+    # on the headline's grouped-query shape (non-causal).
+    "blocksparse_window_b4_hq32_hkv8_n8192_d128": Workload(
+        "blocksparse_window_b4_hq32_hkv8_n8192_d128", 4, 32, 8, 8192, 128, False, 7001,
+        sparse_window=8, sparse_global=1),
 }
+
+SPARSE_BLOCK = 128
+
+
+def window_block_mask(nbq, nbk, window, n_global):
+    """uint8 [1, nbq, nbk]: block (i, j) set iff |i - j| <= window or j < n_global."""
+    i = torch.arange(nbq)[:, None]
+    j = torch.arange(nbk)[None, :]
+    return (((i - j).abs() <= window) | (j < n_global)).to(torch.uint8)[None]
 
 HEADLINE = "gqa_causal_b4_hq32_hkv8_n8192_d128"
 
@@ -138,8 +158,9 @@ def cu_from_lengths(lengths):
 def workload_inputs(w: Workload):
     """All inputs of a workload as CPU tensors, in a dict.
 
-    Padded workloads: q, k, v, seqlens_k (or None).  Packed workloads: q, k, v,
-    cu_seqlens_q, cu_seqlens_k, lengths, max_seqlen.
+    Padded workloads: q, k, v, seqlens_k (or None), and block_mask for the
+    block-sparse ones.  Packed workloads: q, k, v, cu_seqlens_q, cu_seqlens_k,
+    lengths, max_seqlen.
     """
     if w.varlen:
         lengths = make_seqlens(w.varlen_seqs, w.varlen_lo, w.varlen_hi, w.varlen_seed)
@@ -152,5 +173,9 @@ def workload_inputs(w: Workload):
     seqlens = None
     if w.pad_seed is not None:
         seqlens = make_seqlens(w.B, w.pad_lo, w.N, w.pad_seed)
-    return dict(q=q, k=k, v=v, seqlens_k=seqlens)
+    out = dict(q=q, k=k, v=v, seqlens_k=seqlens)
+    if w.sparse:
+        nb = -(-w.N // SPARSE_BLOCK)
+        out["block_mask"] = window_block_mask(nb, nb, w.sparse_window, w.sparse_global)
+    return out
 

@@ -108,6 +108,27 @@ int attn_fwd_dims(const void* q, const void* k, const void* v, void* o, float* l
                   const int32_t* seqlens_k, void* stream);
 
 /*
+ * Block-sparse batched forward (FlashAttention notes (xwysyy),
+ * "Block-Sparse FlashAttention": S = scale Q K^T with the positions of zero
+ * blocks of a block mask set to -inf, then P = softmax(S), O = P V).  The
+ * block mask is applied on top of the causal and padding masks; everything
+ * else (layouts, GQA, seqlens_k, lse, errors) is as for attn_fwd.
+ *   block_mask : device uint8 [mask_heads, ceil(Nq/128), ceil(Nk/128)];
+ *                entry [h][i][j] != 0 lets query rows 128i..128i+127 of head h
+ *                see keys 128j..128j+127.  Shared by every batch element.
+ *   mask_heads : 1 (one mask for every head) or Hq (one per query head);
+ *                otherwise ATTN_ERR_HEADS.
+ * d must be 128 (ATTN_ERR_HEAD_DIM otherwise) and Nk <= 262144
+ * (ATTN_ERR_TOO_LARGE otherwise).  Key tiles of zero blocks are neither
+ * loaded nor computed.  A row whose visible set is empty gets O = 0 and
+ * LSE = -inf.
+ */
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                         const int32_t* seqlens_k, const uint8_t* block_mask, int mask_heads,
+                         void* stream);
+
+/*
  * Packed variable-length forward: num_seqs sequences stored back to back.
  * Sequence z owns query rows cu_seqlens_q[z] .. cu_seqlens_q[z+1]-1 and keys
  * cu_seqlens_k[z] .. cu_seqlens_k[z+1]-1; indices are local to the sequence

@@ -234,3 +234,32 @@ def test_attn_fwd_dims_rejects_bad_arguments(d_qk, d_v, kw, code):
 
 def test_attn_fwd_dims_empty_is_a_noop():
     assert _dims(192, 128, B=0, q=None, k=None, v=None, o=None, lse=None) == attn.ATTN_OK
+
+
+def _bsp(**kw):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4, Hkv=2, Nq=256, Nk=256, d=128,
+             scale=0.088, causal=0, mask=FAKE, mask_heads=1)
+    a.update(kw)
+    return lib.attn_fwd_blocksparse(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]),
+                                    a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                    a["causal"], None, vp(a["mask"]), a["mask_heads"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), attn.ATTN_ERR_NULL),
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(d=64), attn.ATTN_ERR_HEAD_DIM),
+    (dict(mask_heads=2), attn.ATTN_ERR_HEADS),
+    (dict(mask_heads=0), attn.ATTN_ERR_HEADS),
+    (dict(Nk=262145), attn.ATTN_ERR_TOO_LARGE),
+    (dict(o=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(Nq=-1), attn.ATTN_ERR_SIZE),
+])
+def test_attn_fwd_blocksparse_rejects_bad_arguments(kw, code):
+    assert _bsp(**kw) == code
+
+
+def test_attn_fwd_blocksparse_empty_is_a_noop():
+    assert _bsp(B=0, q=None, k=None, v=None, o=None, lse=None, mask=None) == attn.ATTN_OK

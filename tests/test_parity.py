@@ -104,6 +104,53 @@ def test_asymmetric_head_dims_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded):
     assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "(192,128)")
 
 
+SPARSE = [
+    # B, Nq, Nk, Hq, Hkv, causal, padded, mask_heads, density
+    (1, 300, 300, 4, 4, False, False, 1, 0.5),
+    (2, 517, 390, 4, 2, True, False, 4, 0.5),
+    (2, 257, 700, 8, 2, False, True, 8, 0.3),
+    (1, 1000, 1000, 2, 1, True, False, 1, 0.2),
+    (1, 64, 64, 1, 1, False, False, 1, 0.0),
+]
+
+
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal,padded,mh,density", SPARSE)
+def test_blocksparse_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded, mh, density):
+    seed = 7700 + B * 31 + Nq * 7 + Nk + Hq * 3 + int(causal)
+    q, k, v = inputs.make_qkv(B, Nq, Nk, Hq, Hkv, 128, seed, q_mult=2.0)
+    nbq, nbk = -(-Nq // 128), -(-Nk // 128)
+    g = torch.Generator().manual_seed(seed + 3)
+    bm = (torch.rand((mh, nbq, nbk), generator=g) < density).to(torch.uint8)
+    if nbq > 1:
+        bm[:, 1, :] = 0  # a query block with no visible key
+    seqlens = None
+    if padded:
+        seqlens = inputs.make_seqlens(B, 0, Nk, seed + 1)
+    scale = 1.0 / math.sqrt(128)
+    print(f"[parity] block-sparse B={B} Nq={Nq} Nk={Nk} Hq={Hq} causal={causal} heads={mh}",
+          flush=True)
+    o, lse = attn.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), bm.to(DEV), scale, causal,
+                                       None if seqlens is None else seqlens.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward_blocksparse(
+        to_np64(q), to_np64(k), to_np64(v), scale, bm.numpy(), 128, 128, causal,
+        None if seqlens is None else seqlens.numpy(), workers=8)
+    errs = errors(to_np64(o), to_np64(lse), o_ref, lse_ref)
+    assert_parity(errs, "block-sparse")
+    empty = np.isneginf(lse_ref)
+    assert np.isneginf(to_np64(lse)[empty]).all()
+
+
+def test_blocksparse_all_ones_is_the_dense_kernel_bitwise():
+    q, k, v = inputs.make_qkv(2, 600, 600, 8, 2, 128, 7800, q_mult=3.0)
+    bm = torch.ones((1, 5, 5), dtype=torch.uint8, device=DEV)
+    for causal in (False, True):
+        o1, l1 = attn.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), bm, 0.088, causal)
+        o2, l2 = attn.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), 0.088, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_varlen_small_full_oracle():
     lengths = torch.tensor([1, 130, 257, 0, 64, 200], dtype=torch.int32)
     cu = inputs.cu_from_lengths(lengths)
@@ -245,6 +292,10 @@ def test_full_workload_sampled_rows(name):
         plan = attn.attn_varlen_plan(cu, cu, ms, ms, w.causal)
         o2, lse2 = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, ms, ms, w.scale, w.causal,
                                         seq_order=plan)
+    elif w.sparse:
+        bm = x["block_mask"].to(DEV)
+        o, lse = attn.attn_fwd_blocksparse(qd, kd, vd, bm, w.scale, w.causal)
+        o2, lse2 = attn.attn_fwd_blocksparse(qd, kd, vd, bm, w.scale, w.causal)
     else:
         sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(DEV)
         o, lse = attn.attn_fwd(qd, kd, vd, w.scale, w.causal, sl)
@@ -275,6 +326,19 @@ def test_full_workload_sampled_rows(name):
             got_o.append(o_np[a + i, h])
             got_l.append(lse_np[h, a + i])
         errs = errors(np.array(got_o), np.array(got_l), np.array(ref_o), np.array(ref_l))
+    elif w.sparse:
+        samples = sample_rows(rng, w.B, w.Hq, w.N, n_samples)
+        allowed = oracle.block_mask_to_elements(x["block_mask"][0].numpy(), w.N, w.N, 128, 128)
+        G = w.Hq // w.Hkv
+        ref_o, ref_l = [], []
+        for b, h, i in samples:
+            ro, rl = oracle.attention_head(q32[b, :, h], k32[b, :, h // G], v32[b, :, h // G],
+                                           w.scale, w.causal, rows=[i], allowed=allowed)
+            ref_o.append(ro[0])
+            ref_l.append(rl[0])
+        got_o = np.array([o_np[b, i, h] for b, h, i in samples])
+        got_l = np.array([lse_np[b, h, i] for b, h, i in samples])
+        errs = errors(got_o, got_l, np.array(ref_o), np.array(ref_l))
     else:
         samples = sample_rows(rng, w.B, w.Hq, w.N, n_samples)
         sl = None if x["seqlens_k"] is None else x["seqlens_k"].numpy()
