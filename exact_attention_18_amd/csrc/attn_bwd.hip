@@ -14,27 +14,32 @@
 // Three kernels, no atomics, deterministic:
 // * bwd_preprocess: D = <dO, O> per row, and LSE in log2 units (+inf for a
 //   row with no visible key, so exp2(s - lse) is 0 there), into a workspace.
-// * bwd_dkdv_kernel: one workgroup of 4 waves per 128 keys of one (batch, KV
-//   head); wave w owns keys 32w..32w+31 and loops over the G query heads and
-//   32-row query blocks.  S = Q K^T is formed with the keys as the columns of
-//   the 32x32 MFMA accumulator, so each lane holds one key and 16 queries:
-//   P and dS are then B operands (k = queries) of dV^T += dO^T P and
-//   dK^T += Q^T dS without leaving registers; dO^T and Q^T come from gfx950
-//   transpose reads of LDS (ds_read_b64_tr_b16).  The recompute ordering of
-//   FlashAttention-4 (papercache summary), section 3.2.2: iterate along the
-//   KV sequence, values transposed relative to the forward.
-// * bwd_dq_kernel: one workgroup of 4 waves per 128 query rows of one head;
-//   the forward's orientation (S^T = K Q^T, one query per lane), with
-//   dP^T = V dO^T, dS^T = P^T * (dP^T - D) and dQ^T += K^T dS^T.  dQ is
-//   summed over all key blocks inside one workgroup, so it needs neither
-//   atomic adds nor a reduction order (the determinism concern of
-//   FlashAttention-4 (papercache summary), section 3.2.4).
+// * bwd_dkdv_pp_kernel: one workgroup of 8 waves per 128 keys of one (batch,
+//   KV head).  Waves w and w+4 own keys 32(w%4)..+31 and share a SIMD; the two
+//   groups take alternate query steps (32 rows of one of the G query heads)
+//   and alternate MFMA and VALU phases half a period apart.  S = Q K^T is
+//   formed with the keys as the columns of the 32x32 MFMA accumulator, so
+//   each lane holds one key and 16 queries: P and dS are then B operands
+//   (k = queries) of dV^T += dO^T P and dK^T += Q^T dS without leaving
+//   registers; dO^T and Q^T come from gfx950 transpose reads of LDS
+//   (ds_read_b64_tr_b16).  The groups' partial sums are added through LDS
+//   in a fixed order.  The recompute ordering of FlashAttention-4
+//   (papercache summary), section 3.2.2: iterate along the KV sequence,
+//   values transposed relative to the forward.
+// * bwd_dq_pp_kernel: one workgroup of 8 waves per 256 query rows of one
+//   head, the forward's orientation (S^T = K Q^T, one query per lane), with
+//   dP^T = V dO^T, dS^T = P^T * (dP^T - D) and dQ^T += K^T dS^T over key
+//   tiles of 32.  The two wave groups alternate MFMA and VALU phases half a
+//   period apart, as the forward does.  dQ is summed over all key tiles
+//   inside one workgroup, so it needs neither atomic adds nor a reduction
+//   order (the determinism concern of FlashAttention-4 (papercache summary),
+//   section 3.2.4).
 //
-// LDS tiles are row-major rows of d = 128 bf16 (sixteen 16-byte chunks) with
-// chunk c of row r stored at position c ^ swz(r), swz(r) = 4*(r%4) + (r/4)%4.
-// A 32-lane row read (32 rows, one chunk) and a transpose read (4 rows x 2
-// chunks x 4 chunks per half-wave) both touch 16 distinct 16-byte bank
-// groups per 16 lanes, so neither conflicts.
+// LDS tiles hold rows of d = 128 bf16 padded to a pitch of 152 elements
+// (304 bytes): a 16-lane row read and a 32-lane transpose read then touch
+// distinct or at most doubly used banks, and every read is one per-lane base
+// address plus a compile-time offset, which keeps the kernels' address
+// registers few.
 
 #include <hip/hip_runtime.h>
 
@@ -53,8 +58,6 @@ constexpr int kChunks = kD / 8;         // 16-byte chunks per row
 constexpr int kBwThreads = 256;         // 4 waves
 constexpr int kKeysPerWg = 128;         // dK/dV kernel: keys per workgroup
 constexpr int kQStep = 32;              // dK/dV kernel: query rows per step
-constexpr int kQPerWg = 128;            // dQ kernel: query rows per workgroup
-constexpr int kKStep = 64;              // dQ kernel: keys per step
 
 struct BwdParams {
   const __bf16* q;
@@ -73,12 +76,14 @@ struct BwdParams {
   float scale;
 };
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// LDS tile rows are padded to 304 bytes (kPitch elements).  A 16-lane row
+// read (16 rows, one 16-byte chunk) then hits 16 distinct 16-byte bank groups
+// and a 32-lane transpose read at most two lanes per bank, and every read is
+// one per-lane base address plus a compile-time offset.
+constexpr int kPitch = kD + 24;
 
-// Element offset of (row, chunk) in a swizzled tile.
-__device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * kD + 8 * (chunk ^ swz(row));
-}
+// Element offset of (row, 16-byte chunk) in a tile.
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kPitch + 8 * chunk; }
 
 // Row-operand read: lane l takes row r0 + l%32, elements 16*ks + 8*(l/32) .. +7.
 __device__ __forceinline__ bf16x8 read_rows(const __bf16* t, int r0, int ks, int lane) {
@@ -95,7 +100,7 @@ __device__ __forceinline__ bf16x8 read_cols(const __bf16* t, int r0, int d0, int
   return read_tr_pair(t + tile_off(ra, chunk) + sub, t + tile_off(rb, chunk) + sub);
 }
 
-// Global rows [row0, row0 + rows) of a [.., stride] bf16 array -> swizzled LDS tile.
+// Global rows [row0, row0 + rows) of a [.., stride] bf16 array -> padded LDS tile.
 // Loads are 16 bytes per lane, row-contiguous; rows >= valid read as zero.
 template <int ROWS>
 struct TileCopy {
@@ -152,26 +157,39 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const __bf16* o, const __b
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.
+// dK, dV with two wave groups in ping-pong.  8 waves own 128 keys of one
+// (batch, KV head); waves w and w+4 share a SIMD and the same 32 keys, and
+// the two groups take alternate query steps (group g: steps g, g+2, ...).
+// Each wave alternates an MFMA phase -- S and dP of its step i, then dV and
+// dK of its step i-1 from the P and dS it packed in the previous phase --
+// and a VALU phase (P and dS of step i, and the move of its group's next
+// Q / dO tile into LDS); group 1 runs half a period behind group 0, so one
+// wave of each SIMD feeds the matrix core while the other computes (the
+// ping-pong of FlashAttention-4 (papercache summary), section 3.1.2, in
+// CDNA form).  At the end the two groups' partial dK, dV are added through
+// LDS in a fixed order.
+constexpr int kBwPpThreads = 512;
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 k_t[kKeysPerWg * kD];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_t[kKeysPerWg * kD];
-  __shared__ __attribute__((aligned(1024))) __bf16 q_t[2][kQStep * kD];
-  __shared__ __attribute__((aligned(1024))) __bf16 do_t[2][kQStep * kD];
-  __shared__ __attribute__((aligned(16))) float l2_t[2][kQStep];
-  __shared__ __attribute__((aligned(16))) float d_t[2][kQStep];
+__global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) __bf16 kv_t[2 * kKeysPerWg * kPitch];  // K, then V
+  __shared__ __attribute__((aligned(1024))) __bf16 q_t[2][2][kQStep * kPitch];  // [group][buffer]
+  __shared__ __attribute__((aligned(1024))) __bf16 do_t[2][2][kQStep * kPitch];
+  __shared__ __attribute__((aligned(16))) float st_t[2][2][2 * kQStep];       // lse2, then D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int gtid = tid & (kBwThreads - 1);  // thread index within the group
   const int g = lane >> 5;
+  const __bf16* k_t = kv_t;
+  const __bf16* v_t = kv_t + kKeysPerWg * kPitch;
 
-  // work: (batch, KV head) units dealt round-robin to the XCDs, key blocks in order
   const int units = p.B * p.Hkv;
   const int x = blockIdx.x % kXcds, rr = blockIdx.x / kXcds;
   const int u = (rr / p.nblk) * kXcds + x;
-  if (u >= units) return;
+  if (u >= units) return;  // grid padding; uniform over the workgroup
   const int kb = rr % p.nblk;
   const int b = u / p.Hkv, hkv = u % p.Hkv;
   int nk = p.Nk;
@@ -179,85 +197,112 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int k0 = kb * kKeysPerWg;
   const long kv_stride = (long)p.Hkv * kD;
   const long q_stride = (long)p.Hq * kD;
-  const __bf16* kbase = p.k + ((long)b * p.Nk + k0) * kv_stride + (long)hkv * kD;
-  const __bf16* vbase = p.v + ((long)b * p.Nk + k0) * kv_stride + (long)hkv * kD;
 
-  {  // K and V of the block, once
-    TileCopy<kKeysPerWg> kc, vc;
-    kc.load(kbase, kv_stride, min(nk - k0, kKeysPerWg), tid);
-    vc.load(vbase, kv_stride, min(nk - k0, kKeysPerWg), tid);
-    kc.store(k_t, tid);
-    vc.store(v_t, tid);
+  // every tile buffer starts finite (periods without a step multiply zeros by
+  // it); the barrier orders these stores before the first tile stores below
+  for (int i = tid; i < 2 * 2 * kQStep * kPitch / 8; i += kBwPpThreads) {
+    reinterpret_cast<u32x4*>(&q_t[0][0][0])[i] = u32x4{};
+    reinterpret_cast<u32x4*>(&do_t[0][0][0])[i] = u32x4{};
+  }
+  __syncthreads();
+  {  // K (group 0) and V (group 1) of the block
+    TileCopy<kKeysPerWg> c;
+    const __bf16* src = (grp == 0 ? p.k : p.v) + ((long)b * p.Nk + k0) * kv_stride + (long)hkv * kD;
+    c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
+    c.store(kv_t + grp * kKeysPerWg * kPitch, gtid);
   }
 
-  const int wk0 = k0 + wave * 32;         // this wave's first key
-  const int key = wk0 + (lane & 31);      // this lane's key (accumulator column)
+  const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
+  const int key = wk0 + (lane & 31);
   f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
 
-  // query steps: every head of the group, query blocks that can see these keys
   const int s0 = CAUSAL ? (k0 / kQStep) : 0;
   const int nsteps_h = (p.Nq + kQStep - 1) / kQStep - s0;
   const int nsteps = nk > k0 ? max(nsteps_h, 0) * p.G : 0;
+  const int n_mine = (nsteps - grp + 1) / 2;   // this group's steps: grp, grp+2, ...
+  const int n_per = (nsteps + 1) / 2 + 1;      // periods, the same for both groups
+
   TileCopy<kQStep> qc, dc;
-  float stat = 0.f;  // threads 0..63: lse2 (0..31) or delta (32..63) of one row
-  auto fetch = [&](int s) {
-    const int gi = s / nsteps_h, i0 = (s0 + s % nsteps_h) * kQStep;
-    const int h = hkv * p.G + gi;
-    const long rowbase = ((long)b * p.Nq + i0) * q_stride + (long)h * kD;
-    const int valid = min(p.Nq - i0, kQStep);
-    qc.load(p.q + rowbase, q_stride, valid, tid);
-    dc.load(p.dout + rowbase, q_stride, valid, tid);
-    if (tid < 2 * kQStep) {
-      const int i = i0 + (tid & 31);
-      const long sidx = ((long)b * p.Hq + h) * p.Nq + i;
-      stat = (i < p.Nq) ? (tid < kQStep ? p.lse2[sidx] : p.delta[sidx])
-                        : (tid < kQStep ? INFINITY : 0.f);
+  float stat = 0.f;
+  auto step_rows = [&](int i) {  // first query row and head of this group's i-th step
+    const int s = 2 * i + grp;
+    return make_int2((s0 + s % nsteps_h) * kQStep, hkv * p.G + s / nsteps_h);
+  };
+  auto fetch = [&](int i) {
+    const int2 r = step_rows(i);
+    const long rowbase = ((long)b * p.Nq + r.x) * q_stride + (long)r.y * kD;
+    const int valid = min(p.Nq - r.x, kQStep);
+    qc.load(p.q + rowbase, q_stride, valid, gtid);
+    dc.load(p.dout + rowbase, q_stride, valid, gtid);
+    if (gtid < 2 * kQStep) {
+      const int row = r.x + (gtid & 31);
+      const long sidx = ((long)b * p.Hq + r.y) * p.Nq + row;
+      stat = (row < p.Nq) ? (gtid < kQStep ? p.lse2[sidx] : p.delta[sidx])
+                          : (gtid < kQStep ? INFINITY : 0.f);
     }
   };
   auto put = [&](int buf) {
-    qc.store(q_t[buf], tid);
-    dc.store(do_t[buf], tid);
-    if (tid < kQStep) l2_t[buf][tid] = stat;
-    else if (tid < 2 * kQStep) d_t[buf][tid - kQStep] = stat;
+    qc.store(q_t[grp][buf], gtid);
+    dc.store(do_t[grp][buf], gtid);
+    if (gtid < 2 * kQStep) st_t[grp][buf][gtid] = stat;
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (nsteps > 0) {
-    fetch(0);
-    put(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) fetch(s + 1);
-    const int i0 = (s0 + s % nsteps_h) * kQStep;
-    // a wave whose keys all lie after the step's last query sees nothing (causal)
-    const bool live = !CAUSAL || wk0 <= i0 + kQStep - 1;
-    if (live) {
-      const __bf16* qt = q_t[buf];
-      const __bf16* dt = do_t[buf];
-      f32x16 s_acc = {}, dp_acc = {};
+  f32x16 s_acc = {}, dp_acc = {};
+  u32x4 p_pk[2] = {}, ds_pk[2] = {};
+  // One period: MFMA phase, barrier, VALU phase, barrier.
+  auto period = [&](int i, auto par) {
+    constexpr int B0 = decltype(par)::value;  // i % 2: buffer of step i
+    const __bf16* qt = q_t[grp][B0];
+    const __bf16* dt = do_t[grp][B0];
+    const __bf16* qo = q_t[grp][B0 ^ 1];  // step i-1
+    const __bf16* dto = do_t[grp][B0 ^ 1];
+    // ---- MFMA phase
+    s_acc = f32x16{};
+    dp_acc = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        s_acc = mfma32(read_rows(qt, 0, ks, lane), read_rows(k_t, wave * 32, ks, lane), s_acc);
-        dp_acc = mfma32(read_rows(dt, 0, ks, lane), read_rows(v_t, wave * 32, ks, lane), dp_acc);
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      s_acc = mfma32(read_rows(qt, 0, ks, lane), read_rows(k_t, (wave & 3) * 32, ks, lane), s_acc);
+      dp_acc = mfma32(read_rows(dt, 0, ks, lane), read_rows(v_t, (wave & 3) * 32, ks, lane), dp_acc);
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dv_acc[t] = mfma32(read_cols(dto, 16 * qs, 32 * t, lane), __builtin_bit_cast(bf16x8, p_pk[qs]),
+                           dv_acc[t]);
+        dk_acc[t] = mfma32(read_cols(qo, 16 * qs, 32 * t, lane), __builtin_bit_cast(bf16x8, ds_pk[qs]),
+                           dk_acc[t]);
       }
-      // P = exp2(s*c - lse2), dS = P (dP - D); lane: key `key`, queries 8*(r/4)+4g+r%4
-      u32x4 p_pk[2], ds_pk[2];
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    // ---- VALU phase: P, dS of step i (zero when this group has no step i);
+    // this group's step i+1 is loaded meanwhile and stored into the buffer
+    // step i-1 used (its last reader was the MFMA phase just finished)
+    const bool more = i + 1 < n_mine;
+    if (more) fetch(i + 1);
+    if (i < n_mine) {
+      const int i0 = step_rows(i).x;
+      const float* l2t = st_t[grp][B0];
+      const float* ddt = st_t[grp][B0] + kQStep;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi = 8 * r4 + 4 * g;  // first of this group of 4 query rows
-        const float4 l2 = *reinterpret_cast<const float4*>(&l2_t[buf][qi]);
-        const float4 dd = *reinterpret_cast<const float4*>(&d_t[buf][qi]);
+        const int qi = 8 * r4 + 4 * g;
+        const float4 l2 = *reinterpret_cast<const float4*>(l2t + qi);
+        const float4 dd = *reinterpret_cast<const float4*>(ddt + qi);
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
           const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
           const float dv_ = e == 0 ? dd.x : e == 1 ? dd.y : e == 2 ? dd.z : dd.w;
-          const int qrow = i0 + qi + e;
-          const bool vis = key < nk && (!CAUSAL || key <= qrow);
+          const bool vis = key < nk && (!CAUSAL || key <= i0 + qi + e);
           const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -lv)) : 0.f;
           pv[e] = pe;
           dsv[e] = pe * (dp_acc[r] - dv_);
@@ -269,23 +314,60 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         ds_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, d01);
         ds_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (k = the 16 queries of slice qs)
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          dv_acc[t] = mfma32(read_cols(dt, 16 * qs, 32 * t, lane),
-                             __builtin_bit_cast(bf16x8, p_pk[qs]), dv_acc[t]);
-          dk_acc[t] = mfma32(read_cols(qt, 16 * qs, 32 * t, lane),
-                             __builtin_bit_cast(bf16x8, ds_pk[qs]), dk_acc[t]);
-        }
+    } else {
+      p_pk[0] = p_pk[1] = ds_pk[0] = ds_pk[1] = u32x4{};
     }
-    if (s + 1 < nsteps) put(buf ^ 1);
-    __syncthreads();
-  }
+    if (more) put(B0 ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+  };
 
-  // dK = scale * dK^T (transposed back), dV; lane: key `key`, d = 32t + 8*(r/4) + 4g + r%4
-  if (key < p.Nk && key < k0 + kKeysPerWg) {
+  if (n_mine > 0) {
+    fetch(0);
+    put(0);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __syncthreads();
+  if (grp == 1) barrier();  // group 1 runs half a period behind
+  int i = 0;
+  for (; i + 1 < n_per; i += 2) {
+    period(i, std::integral_constant<int, 0>{});
+    period(i + 1, std::integral_constant<int, 1>{});
+  }
+  if (i < n_per) period(i, std::integral_constant<int, 0>{});
+  if (grp == 0) barrier();
+  __syncthreads();
+
+  // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
+  float* red = reinterpret_cast<float*>(kv_t);  // 128 x 128 fp32 = 64 KB, K and V no longer needed
+  const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
+  auto xfer = [&](f32x16* acc, bool add) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4* slot = reinterpret_cast<float4*>(red + kl * kD + 32 * t + 8 * r4 + 4 * g);
+        if (add) {
+          const float4 o = *slot;
+          acc[t][4 * r4 + 0] += o.x;
+          acc[t][4 * r4 + 1] += o.y;
+          acc[t][4 * r4 + 2] += o.z;
+          acc[t][4 * r4 + 3] += o.w;
+        } else {
+          *slot = make_float4(acc[t][4 * r4 + 0], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2],
+                              acc[t][4 * r4 + 3]);
+        }
+      }
+  };
+  if (grp == 1) xfer(dk_acc, false);
+  __syncthreads();
+  if (grp == 0) xfer(dk_acc, true);
+  __syncthreads();
+  if (grp == 1) xfer(dv_acc, false);
+  __syncthreads();
+  if (grp == 0) xfer(dv_acc, true);
+
+  if (grp == 0 && key < p.Nk && key < k0 + kKeysPerWg) {
     __bf16* dkrow = p.dk + ((long)b * p.Nk + key) * kv_stride + (long)hkv * kD;
     __bf16* dvrow = p.dv + ((long)b * p.Nk + key) * kv_stride + (long)hkv * kD;
 #pragma unroll
@@ -306,19 +388,30 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ.
+// dQ with two wave groups in ping-pong: 8 waves own 256 query rows of one
+// head (wave w: rows 32 * (2(w%4) + w/4) .. +31, so the two waves of a SIMD
+// hold adjacent rows); K and V stream in tiles of 32 keys.  Each wave
+// alternates an MFMA phase -- S and dP of tile j, then dQ^T += K^T dS^T of
+// tile j-1 -- and a VALU phase (P, dS of tile j); group 1 runs half a period
+// behind.  Group 0 moves V tiles (two buffers: V_j is read only in phase j),
+// group 1 moves K tiles (four buffers: K_j is read again for dQ one period
+// later); each stores the next tile and loads the one after while its MFMAs
+// run.
+constexpr int kDqTile = 32;
+constexpr int kDqRows = 256;
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(kBwThreads, 1) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 k_t[2][kKStep * kD];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_t[2][kKStep * kD];
+__global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) __bf16 k_t[4][kDqTile * kPitch];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_t[2][kDqTile * kPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int gtid = tid & (kBwThreads - 1);
   const int g = lane >> 5;
 
-  // work: (batch, KV head) units round-robin over XCDs; per unit, query blocks
-  // longest first (causal), query heads of the group innermost
   const int units = p.B * p.Hkv;
   const int per_unit = p.nblk * p.G;
   const int x = blockIdx.x % kXcds, rr = blockIdx.x / kXcds;
@@ -334,9 +427,9 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dq_kernel(BwdParams p) {
 
   const long kv_stride = (long)p.Hkv * kD;
   const long q_stride = (long)p.Hq * kD;
-  const int q0 = qb * kQPerWg;
-  const int qrow = q0 + wave * 32 + (lane & 31);
-  const int wrow0 = q0 + wave * 32;
+  const int q0 = qb * kDqRows;
+  const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);
+  const int qrow = wrow0 + (lane & 31);
   bf16x8 qf[kD / 16], df[kD / 16];
   const long qoff = ((long)b * p.Nq + qrow) * q_stride + (long)h * kD;
 #pragma unroll
@@ -347,76 +440,110 @@ __global__ __launch_bounds__(kBwThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const long sidx = ((long)b * p.Hq + h) * p.Nq + qrow;
   const float l2 = qrow < p.Nq ? p.lse2[sidx] : INFINITY;
   const float dd = qrow < p.Nq ? p.delta[sidx] : 0.f;
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // operands ready before any tile load is in flight
 
   int kv_end = nk;
-  if (CAUSAL) kv_end = min(nk, q0 + kQPerWg);
-  const int ntiles = (kv_end + kKStep - 1) / kKStep;
-  const __bf16* kbase = p.k + (long)b * p.Nk * kv_stride + (long)hkv * kD;
-  const __bf16* vbase = p.v + (long)b * p.Nk * kv_stride + (long)hkv * kD;
+  if (CAUSAL) kv_end = min(nk, q0 + kDqRows);
+  const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
+  const __bf16* src = (grp == 0 ? p.v : p.k) + (long)b * p.Nk * kv_stride + (long)hkv * kD;
+
+  // every buffer starts finite (the first dQ step multiplies zeros by K)
+  for (int i = tid; i < 4 * kDqTile * kPitch / 8; i += kBwPpThreads)
+    reinterpret_cast<u32x4*>(&k_t[0][0])[i] = u32x4{};
+  for (int i = tid; i < 2 * kDqTile * kPitch / 8; i += kBwPpThreads)
+    reinterpret_cast<u32x4*>(&v_t[0][0])[i] = u32x4{};
+  __syncthreads();
+
+  TileCopy<kDqTile> stage;
+  auto fetch = [&](int j) {
+    const int j0 = j * kDqTile;
+    stage.load(src + (long)j0 * kv_stride, kv_stride, min(kv_end - j0, kDqTile), gtid);
+  };
+  auto kbuf = [&](auto I) -> __bf16* { return k_t[decltype(I)::value & 3]; };
+  auto vbuf = [&](auto I) -> __bf16* { return v_t[decltype(I)::value & 1]; };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
-  TileCopy<kKStep> kc, vc;
-  auto fetch = [&](int j) {
-    const int j0 = j * kKStep;
-    kc.load(kbase + (long)j0 * kv_stride, kv_stride, min(kv_end - j0, kKStep), tid);
-    vc.load(vbase + (long)j0 * kv_stride, kv_stride, min(kv_end - j0, kKStep), tid);
-  };
-  if (ntiles > 0) {
-    fetch(0);
-    kc.store(k_t[0], tid);
-    vc.store(v_t[0], tid);
-  }
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) fetch(j + 1);
-    const int j0 = j * kKStep;
-    const bool live = !CAUSAL || j0 <= wrow0 + 31;
-    if (live) {
-      const __bf16* kt = k_t[buf];
-      const __bf16* vt = v_t[buf];
-      u32x4 ds_pk[2][2];  // [32-key block][16-key half]
+  f32x16 s_acc = {}, dp_acc = {};
+  u32x4 ds_pk[2] = {};
+
+  auto period = [&](int j, auto J) {
+    constexpr int j4 = decltype(J)::value;  // j % 4
+    const __bf16* kt = kbuf(std::integral_constant<int, j4>{});
+    const __bf16* vt = vbuf(std::integral_constant<int, j4>{});
+    const __bf16* kto = kbuf(std::integral_constant<int, j4 + 3>{});  // tile j-1
+    // ---- MFMA phase, with this group's tile move after the first MFMAs
+    s_acc = f32x16{};
+    dp_acc = f32x16{};
 #pragma unroll
-      for (int kt2 = 0; kt2 < 2; ++kt2) {
-        f32x16 s_acc = {}, dp_acc = {};
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-          s_acc = mfma32(read_rows(kt, 32 * kt2, ks, lane), qf[ks], s_acc);
-          dp_acc = mfma32(read_rows(vt, 32 * kt2, ks, lane), df[ks], dp_acc);
-        }
-        // lane: query qrow; register r: key j0 + 32*kt2 + 8*(r/4) + 4g + r%4
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float dsv[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int kk = j0 + 32 * kt2 + 8 * ((r + e) >> 2) + 4 * g + ((r + e) & 3);
-            const bool vis = kk < nk && (!CAUSAL || kk <= qrow);
-            const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r + e], p.c, -l2)) : 0.f;
-            dsv[e] = pe * (dp_acc[r + e] - dd);
-          }
-          const bf16x2 pk = {(__bf16)dsv[0], (__bf16)dsv[1]};
-          ds_pk[kt2][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      s_acc = mfma32(read_rows(kt, 0, ks, lane), qf[ks], s_acc);
+      dp_acc = mfma32(read_rows(vt, 0, ks, lane), df[ks], dp_acc);
+      if (ks == 1) {
+        // group 0 stores V_{j+1} over V_{j-1}, group 1 K_{j+1} over K_{j-3}
+        if (j + 1 < n_tiles) {
+          stage.store(grp == 0 ? vbuf(std::integral_constant<int, j4 + 1>{})
+                               : kbuf(std::integral_constant<int, j4 + 1>{}),
+                      gtid);
+          if (j + 2 < n_tiles) fetch(j + 2);
         }
       }
-      // dQ^T += K^T dS^T: A = K^T (32 d x 16 keys) from transpose reads
-#pragma unroll
-      for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[t] = mfma32(read_cols(kt, 32 * kt2 + 16 * hh, 32 * t, lane),
-                            __builtin_bit_cast(bf16x8, ds_pk[kt2][hh]), acc[t]);
     }
-    if (j + 1 < ntiles) {
-      kc.store(k_t[buf ^ 1], tid);
-      vc.store(v_t[buf ^ 1], tid);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = mfma32(read_cols(kto, 16 * hh, 32 * t, lane), __builtin_bit_cast(bf16x8, ds_pk[hh]),
+                        acc[t]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    // ---- VALU phase: P, dS of tile j (zero past the last tile)
+    if (j < n_tiles) {
+      const int j0 = j * kDqTile;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float dsv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int kk = j0 + 8 * ((r + e) >> 2) + 4 * g + ((r + e) & 3);
+          const bool vis = kk < nk && (!CAUSAL || kk <= qrow);
+          const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r + e], p.c, -l2)) : 0.f;
+          dsv[e] = pe * (dp_acc[r + e] - dd);
+        }
+        const bf16x2 pk = {(__bf16)dsv[0], (__bf16)dsv[1]};
+        ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+      }
+    } else {
+      ds_pk[0] = ds_pk[1] = u32x4{};
     }
-    __syncthreads();
+    barrier();
+  };
+
+  if (n_tiles > 0) {
+    fetch(0);
+    stage.store(grp == 0 ? v_t[0] : k_t[0], gtid);
   }
+  if (n_tiles > 1) fetch(1);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __syncthreads();
+  if (grp == 1) barrier();  // group 1 runs half a period behind
+  int j = 0;
+  for (; j + 3 <= n_tiles; j += 4) {
+    period(j, std::integral_constant<int, 0>{});
+    period(j + 1, std::integral_constant<int, 1>{});
+    period(j + 2, std::integral_constant<int, 2>{});
+    period(j + 3, std::integral_constant<int, 3>{});
+  }
+  if (j <= n_tiles) period(j, std::integral_constant<int, 0>{});
+  if (j + 1 <= n_tiles) period(j + 1, std::integral_constant<int, 1>{});
+  if (j + 2 <= n_tiles) period(j + 2, std::integral_constant<int, 2>{});
+  if (grp == 0) barrier();
 
   if (qrow < p.Nq) {
     __bf16* row = p.dq + qoff;
@@ -507,19 +634,22 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     const long grid = units8 * p.nblk;
     if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
     if (causal)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)grid), dim3(kBwThreads), 0, st, p);
+      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<true>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st,
+                         p);
     else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)grid), dim3(kBwThreads), 0, st, p);
+      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<false>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st,
+                         p);
     if (int rc = launched()) return rc;
   }
   if (need_q) {
-    p.nblk = (Nq + kQPerWg - 1) / kQPerWg;
+    p.nblk = (Nq + kDqRows - 1) / kDqRows;
     const long grid = units8 * p.nblk * p.G;
     if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
     if (causal)
-      hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)grid), dim3(kBwThreads), 0, st, p);
+      hipLaunchKernelGGL(bwd_dq_pp_kernel<true>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st, p);
     else
-      hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)grid), dim3(kBwThreads), 0, st, p);
+      hipLaunchKernelGGL(bwd_dq_pp_kernel<false>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st,
+                         p);
     if (int rc = launched()) return rc;
   }
   return ATTN_OK;
