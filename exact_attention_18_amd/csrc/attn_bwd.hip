@@ -76,28 +76,51 @@ struct BwdParams {
   float scale;
 };
 
-// LDS tile rows are padded to 304 bytes (kPitch elements).  A 16-lane row
-// read (16 rows, one 16-byte chunk) then hits 16 distinct 16-byte bank groups
-// and a 32-lane transpose read at most two lanes per bank, and every read is
-// one per-lane base address plus a compile-time offset.
-constexpr int kPitch = kD + 24;
+// LDS tile layout.  Rows (d = 128 bf16, 256 bytes) come in groups of 16; a
+// group spans 272 16-byte units and its row r starts at unit 17 a(r), with
+// a(r) = 4 (r % 4) + r / 4.  Since 17 a(r) = a(r) (mod 16), a 16-lane row
+// read (rows r0..r0+15, one chunk) meets 16 distinct 16-byte bank groups, and
+// a transpose read (rows r0 + 4g + m, m = 0..3, 64 contiguous bytes each)
+// meets 4 (r % 4) + const, four disjoint 64-byte bank ranges: neither
+// conflicts.  Rows are contiguous, so every read is one per-lane base address
+// plus a compile-time offset.
+constexpr int kGroupElems = 16 * 17 * 8;   // elements per group of 16 rows
+constexpr int kRowElems = kGroupElems / 16;  // tile size per row (tiles hold multiples of 16 rows)
+
+// 16-byte unit at which row r (0..15) of a group starts.
+__device__ __forceinline__ int row_slot(int r) { return 17 * (4 * (r & 3) + (r >> 2)); }
 
 // Element offset of (row, 16-byte chunk) in a tile.
-__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kPitch + 8 * chunk; }
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return kGroupElems * (row >> 4) + 8 * (row_slot(row & 15) + chunk);
+}
 
-// Row-operand read: lane l takes row r0 + l%32, elements 16*ks + 8*(l/32) .. +7.
+// Row-operand read: lane l takes row r0 + l%32, elements 16*ks + 8*(l/32) .. +7
+// (r0 a multiple of 16).
 __device__ __forceinline__ bf16x8 read_rows(const __bf16* t, int r0, int ks, int lane) {
-  return *reinterpret_cast<const bf16x8*>(t + tile_off(r0 + (lane & 31), 2 * ks + (lane >> 5)));
+  const int lane_off = kGroupElems * ((lane >> 4) & 1) + 8 * (row_slot(lane & 15) + (lane >> 5));
+  return *reinterpret_cast<const bf16x8*>(t + kGroupElems * (r0 >> 4) + lane_off + 16 * ks);
 }
 
 // Transposed operand: rows r0 + {4g..4g+3} then r0 + {8+4g..8+4g+3} (g = lane/32), as the
-// k-elements, for column d0 + lane%32 of the operand (d0 a multiple of 32).
+// k-elements, for column d0 + lane%32 of the operand (r0 a multiple of 16, d0 of 32).
 __device__ __forceinline__ bf16x8 read_cols(const __bf16* t, int r0, int d0, int lane) {
   const int g = lane >> 5, m = (lane & 15) >> 2, u = lane & 3;
-  const int dcol = d0 + 16 * ((lane >> 4) & 1) + 4 * u;  // first of this lane's 4 columns
-  const int chunk = dcol >> 3, sub = dcol & 7;
-  const int ra = r0 + 4 * g + m, rb = ra + 8;
-  return read_tr_pair(t + tile_off(ra, chunk) + sub, t + tile_off(rb, chunk) + sub);
+  // first of this lane's 4 columns: d0 + 16 ((lane/16) % 2) + 4u
+  const __bf16* base = t + kGroupElems * (r0 >> 4) + d0 + 16 * ((lane >> 4) & 1) + 4 * u;
+  return read_tr_pair(base + 8 * row_slot(4 * g + m), base + 8 * row_slot(8 + 4 * g + m));
+}
+
+// Buffer descriptor over [base, base + bytes), both uniform over the wave.
+// readfirstlane keeps them in scalar registers: a descriptor the compiler
+// leaves in vector registers turns every load through it into a loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), (short)0,
+      __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
 }
 
 // Global rows [row0, row0 + rows) of a [.., stride] bf16 array -> padded LDS tile.
@@ -108,8 +131,7 @@ struct TileCopy {
   static_assert(kPer * kBwThreads == ROWS * kChunks, "tile split");
   u32x4 r[kPer];
   __device__ __forceinline__ void load(const __bf16* base, long stride, int valid, int tid) {
-    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(base), (short)0, max(valid, 0) * (int)(stride * 2), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t res = uniform_rsrc(base, max(valid, 0) * (int)(stride * 2));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + i * kBwThreads;
@@ -172,9 +194,9 @@ constexpr int kBwPpThreads = 512;
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 kv_t[2 * kKeysPerWg * kPitch];  // K, then V
-  __shared__ __attribute__((aligned(1024))) __bf16 q_t[2][2][kQStep * kPitch];  // [group][buffer]
-  __shared__ __attribute__((aligned(1024))) __bf16 do_t[2][2][kQStep * kPitch];
+  __shared__ __attribute__((aligned(1024))) __bf16 kv_t[2 * kKeysPerWg * kRowElems];  // K, then V
+  __shared__ __attribute__((aligned(1024))) __bf16 q_t[2][2][kQStep * kRowElems];  // [group][buffer]
+  __shared__ __attribute__((aligned(1024))) __bf16 do_t[2][2][kQStep * kRowElems];
   __shared__ __attribute__((aligned(16))) float st_t[2][2][2 * kQStep];       // lse2, then D
 
   const int tid = threadIdx.x;
@@ -184,7 +206,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   const int gtid = tid & (kBwThreads - 1);  // thread index within the group
   const int g = lane >> 5;
   const __bf16* k_t = kv_t;
-  const __bf16* v_t = kv_t + kKeysPerWg * kPitch;
+  const __bf16* v_t = kv_t + kKeysPerWg * kRowElems;
 
   const int units = p.B * p.Hkv;
   const int x = blockIdx.x % kXcds, rr = blockIdx.x / kXcds;
@@ -200,7 +222,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
 
   // every tile buffer starts finite (periods without a step multiply zeros by
   // it); the barrier orders these stores before the first tile stores below
-  for (int i = tid; i < 2 * 2 * kQStep * kPitch / 8; i += kBwPpThreads) {
+  for (int i = tid; i < 2 * 2 * kQStep * kRowElems / 8; i += kBwPpThreads) {
     reinterpret_cast<u32x4*>(&q_t[0][0][0])[i] = u32x4{};
     reinterpret_cast<u32x4*>(&do_t[0][0][0])[i] = u32x4{};
   }
@@ -209,7 +231,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     TileCopy<kKeysPerWg> c;
     const __bf16* src = (grp == 0 ? p.k : p.v) + ((long)b * p.Nk + k0) * kv_stride + (long)hkv * kD;
     c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
-    c.store(kv_t + grp * kKeysPerWg * kPitch, gtid);
+    c.store(kv_t + grp * kKeysPerWg * kRowElems, gtid);
   }
 
   const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
@@ -339,6 +361,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   __syncthreads();
 
   // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
+  static_assert(sizeof(kv_t) >= kKeysPerWg * kD * sizeof(float), "reduction buffer");
   float* red = reinterpret_cast<float*>(kv_t);  // 128 x 128 fp32 = 64 KB, K and V no longer needed
   const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
   auto xfer = [&](f32x16* acc, bool add) {
@@ -402,8 +425,8 @@ constexpr int kDqRows = 256;
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 k_t[4][kDqTile * kPitch];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_t[2][kDqTile * kPitch];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_t[4][kDqTile * kRowElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_t[2][kDqTile * kRowElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -448,9 +471,9 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   const __bf16* src = (grp == 0 ? p.v : p.k) + (long)b * p.Nk * kv_stride + (long)hkv * kD;
 
   // every buffer starts finite (the first dQ step multiplies zeros by K)
-  for (int i = tid; i < 4 * kDqTile * kPitch / 8; i += kBwPpThreads)
+  for (int i = tid; i < 4 * kDqTile * kRowElems / 8; i += kBwPpThreads)
     reinterpret_cast<u32x4*>(&k_t[0][0])[i] = u32x4{};
-  for (int i = tid; i < 2 * kDqTile * kPitch / 8; i += kBwPpThreads)
+  for (int i = tid; i < 2 * kDqTile * kRowElems / 8; i += kBwPpThreads)
     reinterpret_cast<u32x4*>(&v_t[0][0])[i] = u32x4{};
   __syncthreads();
 
