@@ -248,9 +248,13 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
 
   TileCopy<kQStep> qc, dc;
   float stat = 0.f;
-  auto step_rows = [&](int i) {  // first query row and head of this group's i-th step
+  // first query row and head of this group's i-th step.  Steps run from the
+  // last query rows back to the first, the G heads of a row block innermost:
+  // the workgroups of one (batch, KV head), which run side by side on one XCD,
+  // then read the same Q and dO rows at about the same time, from L2.
+  auto step_rows = [&](int i) {
     const int s = 2 * i + grp;
-    return make_int2((s0 + s % nsteps_h) * kQStep, hkv * p.G + s / nsteps_h);
+    return make_int2((s0 + nsteps_h - 1 - s / p.G) * kQStep, hkv * p.G + s % p.G);
   };
   auto fetch = [&](int i) {
     const int2 r = step_rows(i);
@@ -278,6 +282,16 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
 
   f32x16 s_acc = {}, dp_acc = {};
   u32x4 p_pk[2] = {}, ds_pk[2] = {};
+  // MFMA phase slices, in groups of four for i = 0..7: S (k-slice i), dV,
+  // dP (k-slice i), dK, the last two for 16 queries qs = i / 4 and 32
+  // dimensions t = i % 4.  S and dP read two row operands each, dV and dK one
+  // transposed operand, so the LDS demand stays even over the phase.  Each
+  // slice's operands are read kAhead slices before its MFMA; scheduling
+  // barriers between the slices keep that order.
+  constexpr int kSlices = 32, kAhead = 2;
+  struct Opnd {
+    bf16x8 a, b;
+  };
   // One period: MFMA phase, barrier, VALU phase, barrier.
   auto period = [&](int i, auto par) {
     constexpr int B0 = decltype(par)::value;  // i % 2: buffer of step i
@@ -285,57 +299,75 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     const __bf16* dt = do_t[grp][B0];
     const __bf16* qo = q_t[grp][B0 ^ 1];  // step i-1
     const __bf16* dto = do_t[grp][B0 ^ 1];
+    const int kr0 = (wave & 3) * 32;
+    auto operand = [&](auto I) __attribute__((always_inline)) -> Opnd {
+      constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
+      if constexpr (kind == 0) return {read_rows(qt, 0, n, lane), read_rows(k_t, kr0, n, lane)};
+      else if constexpr (kind == 2) return {read_rows(dt, 0, n, lane), read_rows(v_t, kr0, n, lane)};
+      else if constexpr (kind == 1) return {read_cols(dto, 16 * (n >> 2), 32 * (n & 3), lane), bf16x8{}};
+      else return {read_cols(qo, 16 * (n >> 2), 32 * (n & 3), lane), bf16x8{}};
+    };
     // ---- MFMA phase
-    s_acc = f32x16{};
-    dp_acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      s_acc = mfma32(read_rows(qt, 0, ks, lane), read_rows(k_t, (wave & 3) * 32, ks, lane), s_acc);
-      dp_acc = mfma32(read_rows(dt, 0, ks, lane), read_rows(v_t, (wave & 3) * 32, ks, lane), dp_acc);
-    }
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dv_acc[t] = mfma32(read_cols(dto, 16 * qs, 32 * t, lane), __builtin_bit_cast(bf16x8, p_pk[qs]),
-                           dv_acc[t]);
-        dk_acc[t] = mfma32(read_cols(qo, 16 * qs, 32 * t, lane), __builtin_bit_cast(bf16x8, ds_pk[qs]),
-                           dk_acc[t]);
-      }
+    Opnd opnd[kAhead];
+    static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
+      opnd[decltype(I)::value] = operand(I);
+    });
+    static_for<0, kSlices>([&](auto I) __attribute__((always_inline)) {
+      constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
+      const Opnd o = opnd[sl % kAhead];
+      if constexpr (sl + kAhead < kSlices) opnd[sl % kAhead] = operand(std::integral_constant<int, sl + kAhead>{});
+      if constexpr (kind == 0)
+        s_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : s_acc);
+      else if constexpr (kind == 2)
+        dp_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : dp_acc);
+      else if constexpr (kind == 1)
+        dv_acc[n & 3] = mfma32(o.a, __builtin_bit_cast(bf16x8, p_pk[n >> 2]), dv_acc[n & 3]);
+      else
+        dk_acc[n & 3] = mfma32(o.a, __builtin_bit_cast(bf16x8, ds_pk[n >> 2]), dk_acc[n & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
     // ---- VALU phase: P, dS of step i (zero when this group has no step i);
     // this group's step i+1 is loaded meanwhile and stored into the buffer
-    // step i-1 used (its last reader was the MFMA phase just finished)
+    // step i-1 used (its last reader was the MFMA phase just finished).  A
+    // step whose rows all see all of this wave's keys skips the mask.
     const bool more = i + 1 < n_mine;
     if (more) fetch(i + 1);
     if (i < n_mine) {
       const int i0 = step_rows(i).x;
       const float* l2t = st_t[grp][B0];
       const float* ddt = st_t[grp][B0] + kQStep;
+      const bool full = wk0 + 32 <= nk && (!CAUSAL || wk0 + 31 <= i0);
+      auto block = [&](bool masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi = 8 * r4 + 4 * g;
-        const float4 l2 = *reinterpret_cast<const float4*>(l2t + qi);
-        const float4 dd = *reinterpret_cast<const float4*>(ddt + qi);
-        float pv[4], dsv[4];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi = 8 * r4 + 4 * g;
+          const float4 l2 = *reinterpret_cast<const float4*>(l2t + qi);
+          const float4 dd = *reinterpret_cast<const float4*>(ddt + qi);
+          float pv[4], dsv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
-          const float dv_ = e == 0 ? dd.x : e == 1 ? dd.y : e == 2 ? dd.z : dd.w;
-          const bool vis = key < nk && (!CAUSAL || key <= i0 + qi + e);
-          const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -lv)) : 0.f;
-          pv[e] = pe;
-          dsv[e] = pe * (dp_acc[r] - dv_);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
+            const float dv_ = e == 0 ? dd.x : e == 1 ? dd.y : e == 2 ? dd.z : dd.w;
+            const bool vis = !masked || (key < nk && (!CAUSAL || key <= i0 + qi + e));
+            const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -lv)) : 0.f;
+            pv[e] = pe;
+            dsv[e] = pe * (dp_acc[r] - dv_);
+          }
+          const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
+          const bf16x2 d01 = {(__bf16)dsv[0], (__bf16)dsv[1]}, d23 = {(__bf16)dsv[2], (__bf16)dsv[3]};
+          p_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, p01);
+          p_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
+          ds_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, d01);
+          ds_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
         }
-        const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
-        const bf16x2 d01 = {(__bf16)dsv[0], (__bf16)dsv[1]}, d23 = {(__bf16)dsv[2], (__bf16)dsv[3]};
-        p_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, p01);
-        p_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
-        ds_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, d01);
-        ds_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
-      }
+      };
+      if (full)
+        block(false);
+      else
+        block(true);
     } else {
       p_pk[0] = p_pk[1] = ds_pk[0] = ds_pk[1] = u32x4{};
     }
@@ -361,15 +393,17 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   __syncthreads();
 
   // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
-  static_assert(sizeof(kv_t) >= kKeysPerWg * kD * sizeof(float), "reduction buffer");
-  float* red = reinterpret_cast<float*>(kv_t);  // 128 x 128 fp32 = 64 KB, K and V no longer needed
+  // [key][d] fp32 with rows padded by 16 bytes, so 16 lanes on 16 keys meet distinct banks
+  constexpr int kRedPitch = kD + 4;
+  static_assert(sizeof(kv_t) >= kKeysPerWg * kRedPitch * sizeof(float), "reduction buffer");
+  float* red = reinterpret_cast<float*>(kv_t);  // K and V are no longer needed
   const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
   auto xfer = [&](f32x16* acc, bool add) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        float4* slot = reinterpret_cast<float4*>(red + kl * kD + 32 * t + 8 * r4 + 4 * g);
+        float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g);
         if (add) {
           const float4 o = *slot;
           acc[t][4 * r4 + 0] += o.x;
@@ -496,19 +530,42 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   f32x16 s_acc = {}, dp_acc = {};
   u32x4 ds_pk[2] = {};
 
+  // MFMA phase slices: 0..15 are S and dP of tile j, alternating (one K or V
+  // row operand each), 16..23 dQ of tile j-1 (one K^T operand each).  Each
+  // slice's LDS operand is read kAhead slices before its MFMA; scheduling
+  // barriers between the slices keep that order.
+  constexpr int kSlices = 24, kAhead = 3, kMoveAt = 3;
   auto period = [&](int j, auto J) {
     constexpr int j4 = decltype(J)::value;  // j % 4
     const __bf16* kt = kbuf(std::integral_constant<int, j4>{});
     const __bf16* vt = vbuf(std::integral_constant<int, j4>{});
     const __bf16* kto = kbuf(std::integral_constant<int, j4 + 3>{});  // tile j-1
-    // ---- MFMA phase, with this group's tile move after the first MFMAs
-    s_acc = f32x16{};
-    dp_acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      s_acc = mfma32(read_rows(kt, 0, ks, lane), qf[ks], s_acc);
-      dp_acc = mfma32(read_rows(vt, 0, ks, lane), df[ks], dp_acc);
-      if (ks == 1) {
+    auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < 16) return read_rows((i & 1) ? vt : kt, 0, i >> 1, lane);
+      else return read_cols(kto, 16 * ((i - 16) >> 2), 32 * ((i - 16) & 3), lane);
+    };
+    // ---- MFMA phase, with this group's tile move after slice kMoveAt
+    bf16x8 opnd[kAhead];
+    static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
+      opnd[decltype(I)::value] = operand(I);
+    });
+    static_for<0, kSlices>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      const bf16x8 a = opnd[i % kAhead];
+      if constexpr (i + kAhead < kSlices) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
+      if constexpr (i < 16) {
+        constexpr int ks = i >> 1;
+        if constexpr (i & 1)
+          dp_acc = mfma32(a, df[ks], ks == 0 ? f32x16{} : dp_acc);
+        else
+          s_acc = mfma32(a, qf[ks], ks == 0 ? f32x16{} : s_acc);
+      } else {
+        constexpr int hh = (i - 16) >> 2, t = (i - 16) & 3;
+        acc[t] = mfma32(a, __builtin_bit_cast(bf16x8, ds_pk[hh]), acc[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == kMoveAt) {
         // group 0 stores V_{j+1} over V_{j-1}, group 1 K_{j+1} over K_{j-3}
         if (j + 1 < n_tiles) {
           stage.store(grp == 0 ? vbuf(std::integral_constant<int, j4 + 1>{})
@@ -516,31 +573,34 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
                       gtid);
           if (j + 2 < n_tiles) fetch(j + 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[t] = mfma32(read_cols(kto, 16 * hh, 32 * t, lane), __builtin_bit_cast(bf16x8, ds_pk[hh]),
-                        acc[t]);
+    });
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
-    // ---- VALU phase: P, dS of tile j (zero past the last tile)
+    // ---- VALU phase: P, dS of tile j (zero past the last tile).  A tile whose
+    // keys all are visible to all of this wave's rows skips the mask.
     if (j < n_tiles) {
       const int j0 = j * kDqTile;
+      const bool full = j0 + kDqTile <= nk && (!CAUSAL || j0 + kDqTile - 1 <= wrow0);
+      auto dsval = [&](int r, bool masked) __attribute__((always_inline)) {
+        const int kk = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool vis = !masked || (kk < nk && (!CAUSAL || kk <= qrow));
+        const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -l2)) : 0.f;
+        return pe * (dp_acc[r] - dd);
+      };
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float dsv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int kk = j0 + 8 * ((r + e) >> 2) + 4 * g + ((r + e) & 3);
-          const bool vis = kk < nk && (!CAUSAL || kk <= qrow);
-          const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r + e], p.c, -l2)) : 0.f;
-          dsv[e] = pe * (dp_acc[r + e] - dd);
+        for (int r = 0; r < 16; r += 2) {
+          const bf16x2 pk = {(__bf16)dsval(r, false), (__bf16)dsval(r + 1, false)};
+          ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
         }
-        const bf16x2 pk = {(__bf16)dsv[0], (__bf16)dsv[1]};
-        ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const bf16x2 pk = {(__bf16)dsval(r, true), (__bf16)dsval(r + 1, true)};
+          ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+        }
       }
     } else {
       ds_pk[0] = ds_pk[1] = u32x4{};
