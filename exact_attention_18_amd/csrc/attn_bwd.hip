@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   // transposed operand, so the LDS demand stays even over the phase.  Each
   // slice's operands are read kAhead slices before its MFMA; scheduling
   // barriers between the slices keep that order.
-  constexpr int kSlices = 32, kAhead = 2;
+  constexpr int kSlices = 32, kAhead = 3;
   struct Opnd {
     bf16x8 a, b;
   };
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   // row operand each), 16..23 dQ of tile j-1 (one K^T operand each).  Each
   // slice's LDS operand is read kAhead slices before its MFMA; scheduling
   // barriers between the slices keep that order.
-  constexpr int kSlices = 24, kAhead = 3, kMoveAt = 3;
+  constexpr int kSlices = 24, kAhead = 4, kMoveAt = 12;
   auto period = [&](int j, auto J) {
     constexpr int j4 = decltype(J)::value;  // j % 4
     const __bf16* kt = kbuf(std::integral_constant<int, j4>{});
