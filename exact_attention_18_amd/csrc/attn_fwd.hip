@@ -848,7 +848,11 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         }
       }
     };
+    // The wave in its MFMA phase gets issue priority over the other wave of
+    // its SIMD, so a ready MFMA is not held behind that wave's softmax.
+    __builtin_amdgcn_s_setprio(3);
     mphase(kbuf(std::integral_constant<int, j2>{}), vbuf(std::integral_constant<int, j2 + 1>{}), move);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this phase's LDS stores are done
     barrier();
     if (j < n_iter) vphase(j);
