@@ -147,6 +147,21 @@ def cpu_baseline(w, x, target_s: float):
                       f"and P materialised, {workers} threads, {t_total:.1f} s wall"}
 
 
+def warm_up(step, n):
+    """Runs n untimed warm-up steps; returns the first one's time in ms (cold caches), or None."""
+    if n <= 0:
+        return None
+    f_s, f_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f_s.record()
+    step()
+    f_e.record()
+    for _ in range(n - 1):
+        step()
+    torch.cuda.synchronize()
+    return round(f_s.elapsed_time(f_e), 5)
+
+
 def bench_backward(args, w, x, dev, fwd_flops):
     """Times attn_bwd on the workload (FLOPs: 2.5x the forward, as the pages count them)."""
     if w.varlen or w.sparse or w.d != 128 or w.d_v != 128:
@@ -163,9 +178,7 @@ def bench_backward(args, w, x, dev, fwd_flops):
     def step():
         attn.attn_bwd(q, k, v, o, lse, do, w.scale, w.causal, sl, workspace=ws, out=(dq, dk, dv))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    first_ms = warm_up(step, args.warmup)
     K = args.steps
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -182,7 +195,8 @@ def bench_backward(args, w, x, dev, fwd_flops):
     line = {
         "metric": "attn bwd TFLOP/s bf16 hd128 (2.5x forward FLOPs)",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "first_run_ms": first_ms,
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded i.i.d. N(0,1) bf16; dO seeded likewise)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
@@ -238,9 +252,7 @@ def main():
         return bench_backward(args, w, x, dev, flops)
     step = make_step(w, x, dev)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    first_ms = warm_up(step, args.warmup)
     K = args.steps
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -256,7 +268,9 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]))
+    per_step = [a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]
+    kernel_ms = float(np.mean(per_step))
+    median_ms = float(np.median(per_step))
     print(f"[bench] {K} steps, {ms_step:.4f} ms/step, kernel {kernel_ms:.4f} ms", file=sys.stderr,
           flush=True)
 
@@ -277,6 +291,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(median_ms, 5),
+        "first_run_ms": first_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
