@@ -668,8 +668,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   }
   const __bf16* gbase = fetch_v ? vbase : kbase;
   u32x4 stage[CH];
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const int kv0 = tile_of(t) * T::BC;
+  // loads key tile `tile` (an index into the key sequence, not into the work list)
+  auto load_tile_at = [&](int tile) __attribute__((always_inline)) {
+    const int kv0 = tile * T::BC;
     const int nrows = min(kv_end - kv0, T::BC);
     const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16*>(gbase + (long)kv0 * (row_bytes / 2)), (short)0, nrows * (int)row_bytes,
@@ -813,11 +814,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
   // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
   // V_j at h = 2j+1, group 1 runs M_j at h = 2j+1 and V_j at h = 2j+2.  K_t
-  // lives in k[t%2], V_t in v[t%2].  Tiles move global -> VGPRs -> LDS in
-  // the MFMA phases, between two MFMAs: during M_j group 0 stores V_j
-  // (loaded during M_{j-1}) and loads V_{j+1}; group 1 stores K_{j+1} and
-  // loads K_{j+2}.  Each store is complete before the barrier that ends its
-  // phase, which precedes the first read of the tile.
+  // lives in k[t%2], V_t in v[t%2].  Tiles move global -> VGPRs -> LDS:
+  // during M_j, between two MFMAs, group 0 stores V_j (loaded one period
+  // earlier) and group 1 stores K_{j+1}; at the start of V_j (block-sparse:
+  // at the end of M_j) they load V_{j+1} and K_{j+2}.  Each store is complete before the barrier that
+  // ends its phase, which precedes the first read of the tile.
+  constexpr bool kLoadInMfmaPhase = SPARSE;
   auto kbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
     if constexpr (decltype(I)::value % 2 == 0) return k_lds0; else return k_lds1;
   };
@@ -835,16 +837,21 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   auto period = [&](int j, auto J) __attribute__((always_inline)) {
     constexpr int j2 = decltype(J)::value;  // j % 2
     const int st = fetch_v ? j : j + 1;  // tile stored in this phase
+    // the tile loaded at the start of the VALU phase; looked up now, so that a
+    // work-list read (block-sparse) is done by then
+    const int next_tile = st + 1 < n_iter ? tile_of(st + 1) : 0;
     __bf16* dst = fetch_v ? vbuf(std::integral_constant<int, j2>{}) : kbuf(std::integral_constant<int, j2 + 1>{});
     // The staged tile goes to LDS one 16-byte chunk per lane at a time,
-    // spread over the phase; after the last chunk the next tile is loaded
-    // into the freed registers.
+    // spread over the MFMA phase; the next tile is loaded into the freed
+    // registers at the start of the VALU phase, which is the shorter one
+    // (dense), or right after the last chunk (block-sparse, whose VALU phase
+    // masks more tiles: there the MFMA-phase placement measured faster).
     auto move = [&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
       if (st < n_iter) {
         if (c < nch) store_chunk(dst, C);
-        if constexpr (c == CH - 1) {
-          if (st + 1 < n_iter) load_tile(st + 1);
+        if constexpr (kLoadInMfmaPhase && c == CH - 1) {
+          if (st + 1 < n_iter) load_tile_at(next_tile);
         }
       }
     };
@@ -855,6 +862,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this phase's LDS stores are done
     barrier();
+    if constexpr (!kLoadInMfmaPhase) {
+      if (st + 1 < n_iter) load_tile_at(next_tile);
+    }
     if (j < n_iter) vphase(j);
     barrier();
   };
@@ -865,10 +875,10 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
   // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
   if (fetch_v) {
-    if (n_iter > 0) load_tile(0);
+    if (n_iter > 0) load_tile_at(tile_of(0));
   } else {
-    if (n_iter > 0) { load_tile(0); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
-    if (n_iter > 1) load_tile(1);
+    if (n_iter > 0) { load_tile_at(tile_of(0)); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
+    if (n_iter > 1) load_tile_at(tile_of(1));
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   barrier();
