@@ -802,7 +802,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         ls0 += e0;
         ls1 += e1;
         const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-        pv_op[kt][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+        uint32_t u = __builtin_bit_cast(uint32_t, pk);
+        asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
+        pv_op[kt][r >> 3][(r & 7) >> 1] = u;
       }
     asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
     l_run = l_run * alpha + (ls0 + ls1);
@@ -846,13 +848,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     // registers at the start of the VALU phase, which is the shorter one
     // (dense), or right after the last chunk (block-sparse, whose VALU phase
     // masks more tiles: there the MFMA-phase placement measured faster).
+    // Past the last tile the store is left unguarded: it writes stale
+    // registers into a buffer no later MFMA phase reads.
     auto move = [&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
-      if (st < n_iter) {
-        if (c < nch) store_chunk(dst, C);
-        if constexpr (kLoadInMfmaPhase && c == CH - 1) {
-          if (st + 1 < n_iter) load_tile_at(next_tile);
-        }
+      if (c < nch) store_chunk(dst, C);
+      if constexpr (kLoadInMfmaPhase && c == CH - 1) {
+        if (st + 1 < n_iter) load_tile_at(next_tile);
       }
     };
     // The wave in its MFMA phase gets issue priority over the other wave of
