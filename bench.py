@@ -164,19 +164,35 @@ def warm_up(step, n):
 
 def bench_backward(args, w, x, dev, fwd_flops):
     """Times attn_bwd on the workload (FLOPs: 2.5x the forward, as the pages count them)."""
-    if w.varlen or w.sparse or w.d != 128 or w.d_v != 128:
-        print("the backward covers the batched dense d=128 workloads", file=sys.stderr)
+    if w.sparse or w.d != 128 or w.d_v != 128:
+        print("the backward covers the dense d=128 workloads", file=sys.stderr)
         sys.exit(2)
     q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
-    sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
-    o, lse = attn.attn_fwd(q, k, v, w.scale, w.causal, sl)
     do = inputs.make_dout(x["q"].shape, w.seed + 77).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((attn.load_library().attn_bwd_workspace_size(w.B, w.Hq, w.N),),
-                     dtype=torch.uint8, device=dev)
+    lib = attn.load_library()
+    if w.varlen:
+        # packed: the LPT plan and the backward, as the forward's step runs plan + forward
+        cq, ck, mx = x["cu_seqlens_q"].to(dev), x["cu_seqlens_k"].to(dev), x["max_seqlen"]
+        order = torch.empty((cq.numel() - 1,), dtype=torch.int32, device=dev)
+        attn.attn_varlen_plan(cq, ck, mx, mx, w.causal, out=order)
+        o, lse = attn.attn_fwd_varlen(q, k, v, cq, ck, mx, mx, w.scale, w.causal, seq_order=order)
+        ws = torch.empty((lib.attn_bwd_workspace_size(1, w.Hq, q.shape[0]),), dtype=torch.uint8,
+                         device=dev)
 
-    def step():
-        attn.attn_bwd(q, k, v, o, lse, do, w.scale, w.causal, sl, workspace=ws, out=(dq, dk, dv))
+        def step():
+            attn.attn_varlen_plan(cq, ck, mx, mx, w.causal, out=order)
+            attn.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, mx, mx, w.scale, w.causal,
+                                 seq_order=order, workspace=ws, out=(dq, dk, dv))
+    else:
+        sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
+        o, lse = attn.attn_fwd(q, k, v, w.scale, w.causal, sl)
+        ws = torch.empty((lib.attn_bwd_workspace_size(w.B, w.Hq, w.N),), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            attn.attn_bwd(q, k, v, o, lse, do, w.scale, w.causal, sl, workspace=ws,
+                          out=(dq, dk, dv))
 
     first_ms = warm_up(step, args.warmup)
     K = args.steps

@@ -30,7 +30,8 @@ ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
 
-EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen", "attn_varlen_plan", "attn_bwd", "attn_bwd_workspace_size",
+EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen", "attn_varlen_plan",
+           "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_size",
            "attn_strerror", "attn_last_hip_error", "attn_version")
 
 _lib = None
@@ -62,6 +63,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                              f32, i32, vp, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                    i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_bwd_varlen.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [i32]
@@ -287,6 +291,70 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                       _ptr(dv), _ptr(workspace), B, Hq, Hkv, Nq, Nk, d, float(scale),
                       int(bool(causal)), _ptr(seqlens_k), _stream_handle(dev))
     _check(rc, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    lse: torch.Tensor, dout: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                    scale: Optional[float] = None, causal: bool = False,
+                    seq_order: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV (bf16) of the packed forward (attn_fwd_varlen) from its O and LSE.
+
+    q, o, dout [Tq,Hq,d]; k, v [Tk,Hkv,d]; lse [Hq,Tq] as attn_fwd_varlen
+    returns it; d must be 128.  Rows and keys that belong to no sequence are
+    not written (zero when dq, dk, dv are allocated here).
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("expected q, o, dout [Tq,Hq,d] and k, v [Tk,Hkv,d]")
+    Tq, Hq, d = q.shape
+    _, Hkv, dk_ = k.shape
+    if dk_ != d:
+        raise ValueError("q and k disagree on head dim")
+    if lse.shape != (Hq, Tq):
+        raise ValueError("lse must have shape [Hq,Tq]")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of equal length")
+    num_seqs = cu_seqlens_q.numel() - 1
+    if seq_order is not None:
+        _need(seq_order, "seq_order", torch.int32, dev)
+        if seq_order.shape != (num_seqs,):
+            raise ValueError("seq_order must have shape [num_seqs]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(lib.attn_bwd_workspace_size(1, Hq, Tq))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+    if out is None:
+        dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    else:
+        dq, dk, dv = out
+        _need(dq, "dq", torch.bfloat16, dev)
+        _need(dk, "dk", torch.bfloat16, dev)
+        _need(dv, "dv", torch.bfloat16, dev)
+        if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
+            raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    rc = lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(workspace), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), num_seqs, Tq, Hq, Hkv, int(max_seqlen_q),
+                             int(max_seqlen_k), d, float(scale), int(bool(causal)),
+                             _ptr(seq_order), _stream_handle(dev))
+    _check(rc, "attn_bwd_varlen")
     return dq, dk, dv
 
 

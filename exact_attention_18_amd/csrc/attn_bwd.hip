@@ -69,12 +69,61 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  const int32_t* seqlens_k;
-  int B, Hq, Hkv, G, Nq, Nk;
+  const int32_t* seqlens_k;   // batched form: valid keys per batch element, may be null
+  const int32_t* cu_q;        // packed form: sequence offsets into the rows, else null
+  const int32_t* cu_k;
+  const int32_t* seq_order;   // packed form: work order of the sequences, may be null
+  int B, Hq, Hkv, G, Nq, Nk;  // packed form: B = sequences, Nq/Nk = the longest lengths
+  long Tq;                    // packed form: total query rows (the LSE row stride per head)
   int nblk;             // key blocks (dK/dV) or query blocks (dQ) per (batch, head)
   float c;              // scale * log2(e)
   float scale;
 };
+
+// Rows of one work unit (batch element, or sequence of a packed batch).
+struct UnitRows {
+  long q0, k0;    // first query / key row in the row-major arrays
+  int nq, nk;     // valid queries and keys
+  int k_write;    // keys whose dK, dV rows this unit writes
+  long lse0;      // LSE / D index of (head 0, row 0); head h adds lse_h * h
+  long lse_h;
+};
+
+__device__ __forceinline__ UnitRows unit_rows(const BwdParams& p, int b) {
+  UnitRows r;
+  if (p.cu_q != nullptr) {
+    const int z = p.seq_order != nullptr ? min(max(p.seq_order[b], 0), p.B - 1) : b;
+    r.q0 = min(max(p.cu_q[z], 0), (int)p.Tq);  // rows stay inside the total_q rows
+    r.k0 = p.cu_k[z];
+    r.nq = min(min(max(p.cu_q[z + 1] - p.cu_q[z], 0), p.Nq), (int)(p.Tq - r.q0));
+    r.nk = min(max(p.cu_k[z + 1] - p.cu_k[z], 0), p.Nk);
+    r.k_write = r.nk;
+    r.lse0 = r.q0;
+    r.lse_h = p.Tq;
+  } else {
+    r.q0 = (long)b * p.Nq;
+    r.k0 = (long)b * p.Nk;
+    r.nq = p.Nq;
+    r.nk = p.seqlens_k != nullptr ? min(max(p.seqlens_k[b], 0), p.Nk) : p.Nk;
+    r.k_write = p.Nk;  // padded keys get zero gradients
+    r.lse0 = (long)b * p.Hq * p.Nq;
+    r.lse_h = p.Nq;
+  }
+  // all uniform over the workgroup: keep them in scalar registers
+  auto u64 = [](long x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return static_cast<long>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  r.q0 = u64(r.q0);
+  r.k0 = u64(r.k0);
+  r.lse0 = u64(r.lse0);
+  r.lse_h = u64(r.lse_h);
+  r.nq = __builtin_amdgcn_readfirstlane(r.nq);
+  r.nk = __builtin_amdgcn_readfirstlane(r.nk);
+  r.k_write = __builtin_amdgcn_readfirstlane(r.k_write);
+  return r;
+}
 
 // LDS tile layout.  Rows (d = 128 bf16, 256 bytes) come in groups of 16; a
 // group spans 272 16-byte units and its row r starts at unit 17 a(r), with
@@ -151,9 +200,13 @@ struct TileCopy {
 
 // ---------------------------------------------------------------------------
 // D = <dO, O> and LSE in log2 units, one row per 16 lanes.
+// Packed form (B = 1, Nq = total rows): lse_rows points at the forward's LSE
+// row count per head (cu_seqlens_q[num_seqs]); rows past it belong to no
+// sequence and are skipped.  Batched form: lse_rows is null.
 __global__ __launch_bounds__(256) void bwd_preprocess(const __bf16* o, const __bf16* dout,
                                                       const float* lse, float* lse2, float* delta,
-                                                      int B, int Hq, int Nq) {
+                                                      int B, int Hq, int Nq,
+                                                      const int32_t* lse_rows) {
   const long rows = (long)B * Nq * Hq;
   const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);  // row of [B, Nq, Hq]
   const int sub = threadIdx.x & 15;
@@ -172,7 +225,13 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const __bf16* o, const __b
     const int i = (int)(bi % Nq);
     const int b = (int)(bi / Nq);
     const long out = ((long)b * Hq + h) * Nq + i;
-    const float l = lse[out];
+    long in = out;
+    if (lse_rows != nullptr) {
+      const int n = min(max(*lse_rows, 0), Nq);
+      if (i >= n) return;
+      in = (long)h * n + i;
+    }
+    const float l = lse[in];
     delta[out] = acc;
     lse2[out] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
@@ -214,9 +273,10 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   if (u >= units) return;  // grid padding; uniform over the workgroup
   const int kb = rr % p.nblk;
   const int b = u / p.Hkv, hkv = u % p.Hkv;
-  int nk = p.Nk;
-  if (p.seqlens_k != nullptr) nk = min(max(p.seqlens_k[b], 0), p.Nk);
+  const UnitRows ur = unit_rows(p, b);
+  const int nk = ur.nk, nq = ur.nq;
   const int k0 = kb * kKeysPerWg;
+  if (k0 >= ur.k_write) return;  // a packed sequence shorter than the longest; uniform
   const long kv_stride = (long)p.Hkv * kD;
   const long q_stride = (long)p.Hq * kD;
 
@@ -229,7 +289,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   __syncthreads();
   {  // K (group 0) and V (group 1) of the block
     TileCopy<kKeysPerWg> c;
-    const __bf16* src = (grp == 0 ? p.k : p.v) + ((long)b * p.Nk + k0) * kv_stride + (long)hkv * kD;
+    const __bf16* src = (grp == 0 ? p.k : p.v) + (ur.k0 + k0) * kv_stride + (long)hkv * kD;
     c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
     c.store(kv_t + grp * kKeysPerWg * kRowElems, gtid);
   }
@@ -241,7 +301,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   for (int t = 0; t < 4; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
 
   const int s0 = CAUSAL ? (k0 / kQStep) : 0;
-  const int nsteps_h = (p.Nq + kQStep - 1) / kQStep - s0;
+  const int nsteps_h = (nq + kQStep - 1) / kQStep - s0;
   const int nsteps = nk > k0 ? max(nsteps_h, 0) * p.G : 0;
   const int n_mine = (nsteps - grp + 1) / 2;   // this group's steps: grp, grp+2, ...
   const int n_per = (nsteps + 1) / 2 + 1;      // periods, the same for both groups
@@ -258,14 +318,14 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   };
   auto fetch = [&](int i) {
     const int2 r = step_rows(i);
-    const long rowbase = ((long)b * p.Nq + r.x) * q_stride + (long)r.y * kD;
-    const int valid = min(p.Nq - r.x, kQStep);
+    const long rowbase = (ur.q0 + r.x) * q_stride + (long)r.y * kD;
+    const int valid = min(nq - r.x, kQStep);
     qc.load(p.q + rowbase, q_stride, valid, gtid);
     dc.load(p.dout + rowbase, q_stride, valid, gtid);
     if (gtid < 2 * kQStep) {
       const int row = r.x + (gtid & 31);
-      const long sidx = ((long)b * p.Hq + r.y) * p.Nq + row;
-      stat = (row < p.Nq) ? (gtid < kQStep ? p.lse2[sidx] : p.delta[sidx])
+      const long sidx = ur.lse0 + ur.lse_h * r.y + row;
+      stat = (row < nq) ? (gtid < kQStep ? p.lse2[sidx] : p.delta[sidx])
                           : (gtid < kQStep ? INFINITY : 0.f);
     }
   };
@@ -424,9 +484,9 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   __syncthreads();
   if (grp == 0) xfer(dv_acc, true);
 
-  if (grp == 0 && key < p.Nk && key < k0 + kKeysPerWg) {
-    __bf16* dkrow = p.dk + ((long)b * p.Nk + key) * kv_stride + (long)hkv * kD;
-    __bf16* dvrow = p.dv + ((long)b * p.Nk + key) * kv_stride + (long)hkv * kD;
+  if (grp == 0 && key < ur.k_write && key < k0 + kKeysPerWg) {
+    __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * kD;
+    __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * kD;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -479,30 +539,31 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   const int qb = CAUSAL ? (p.nblk - 1 - qbi) : qbi;
   const int b = u / p.Hkv, hkv = u % p.Hkv;
   const int h = hkv * p.G + gi;
-  int nk = p.Nk;
-  if (p.seqlens_k != nullptr) nk = min(max(p.seqlens_k[b], 0), p.Nk);
+  const UnitRows ur = unit_rows(p, b);
+  const int nk = ur.nk, nq = ur.nq;
 
   const long kv_stride = (long)p.Hkv * kD;
   const long q_stride = (long)p.Hq * kD;
   const int q0 = qb * kDqRows;
+  if (q0 >= nq) return;  // a packed sequence shorter than the longest; uniform
   const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);
   const int qrow = wrow0 + (lane & 31);
   bf16x8 qf[kD / 16], df[kD / 16];
-  const long qoff = ((long)b * p.Nq + qrow) * q_stride + (long)h * kD;
+  const long qoff = (ur.q0 + qrow) * q_stride + (long)h * kD;
 #pragma unroll
   for (int ks = 0; ks < kD / 16; ++ks) {
-    qf[ks] = qrow < p.Nq ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * g) : bf16x8{};
-    df[ks] = qrow < p.Nq ? *reinterpret_cast<const bf16x8*>(p.dout + qoff + 16 * ks + 8 * g) : bf16x8{};
+    qf[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * g) : bf16x8{};
+    df[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.dout + qoff + 16 * ks + 8 * g) : bf16x8{};
   }
-  const long sidx = ((long)b * p.Hq + h) * p.Nq + qrow;
-  const float l2 = qrow < p.Nq ? p.lse2[sidx] : INFINITY;
-  const float dd = qrow < p.Nq ? p.delta[sidx] : 0.f;
+  const long sidx = ur.lse0 + ur.lse_h * h + qrow;
+  const float l2 = qrow < nq ? p.lse2[sidx] : INFINITY;
+  const float dd = qrow < nq ? p.delta[sidx] : 0.f;
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // operands ready before any tile load is in flight
 
   int kv_end = nk;
   if (CAUSAL) kv_end = min(nk, q0 + kDqRows);
   const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
-  const __bf16* src = (grp == 0 ? p.v : p.k) + (long)b * p.Nk * kv_stride + (long)hkv * kD;
+  const __bf16* src = (grp == 0 ? p.v : p.k) + ur.k0 * kv_stride + (long)hkv * kD;
 
   // every buffer starts finite (the first dQ step multiplies zeros by K)
   for (int i = tid; i < 4 * kDqTile * kRowElems / 8; i += kBwPpThreads)
@@ -628,7 +689,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   if (j + 2 <= n_tiles) period(j + 2, std::integral_constant<int, 2>{});
   if (grp == 0) barrier();
 
-  if (qrow < p.Nq) {
+  if (qrow < nq) {
     __bf16* row = p.dq + qoff;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -649,6 +710,47 @@ int launched() {
   if (e != hipSuccess) {
     attn_detail::last_hip_error = static_cast<int>(e);
     return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+// Launches preprocess, dK/dV and dQ for the units p describes.  The LSE and
+// D workspace rows are [pre_b, Hq, pre_nq] (batched: B, Nq; packed: 1, Tq).
+int launch_backward(BwdParams p, const __bf16* o, const float* lse, int pre_b, long pre_nq,
+                    const int32_t* lse_rows, bool need_q, bool need_k, bool causal,
+                    hipStream_t st) {
+  const long units8 = ((long)p.B * p.Hkv + kXcds - 1) / kXcds * kXcds;
+  const int nblk_k = (p.Nk + kKeysPerWg - 1) / kKeysPerWg;
+  const int nblk_q = (p.Nq + kDqRows - 1) / kDqRows;
+  const long grid_k = units8 * nblk_k, grid_q = units8 * nblk_q * p.G;
+  const long rows = (long)pre_b * pre_nq * p.Hq;
+  if (grid_k > INT_MAX || grid_q > INT_MAX || (rows + 15) / 16 > INT_MAX) return ATTN_ERR_TOO_LARGE;
+  float* lse2 = const_cast<float*>(p.lse2);
+  float* delta = const_cast<float*>(p.delta);
+  if (need_q) {
+    hipLaunchKernelGGL(bwd_preprocess, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, o,
+                       p.dout, lse, lse2, delta, pre_b, p.Hq, (int)pre_nq, lse_rows);
+    if (int rc = launched()) return rc;
+  }
+  if (need_k) {
+    p.nblk = nblk_k;
+    if (causal)
+      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<true>, dim3((unsigned)grid_k), dim3(kBwPpThreads), 0,
+                         st, p);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<false>, dim3((unsigned)grid_k), dim3(kBwPpThreads), 0,
+                         st, p);
+    if (int rc = launched()) return rc;
+  }
+  if (need_q) {
+    p.nblk = nblk_q;
+    if (causal)
+      hipLaunchKernelGGL(bwd_dq_pp_kernel<true>, dim3((unsigned)grid_q), dim3(kBwPpThreads), 0, st,
+                         p);
+    else
+      hipLaunchKernelGGL(bwd_dq_pp_kernel<false>, dim3((unsigned)grid_q), dim3(kBwPpThreads), 0,
+                         st, p);
+    if (int rc = launched()) return rc;
   }
   return ATTN_OK;
 }
@@ -705,36 +807,59 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.Nk = Nk;
   p.scale = scale;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  const long units8 = ((long)B * Hkv + kXcds - 1) / kXcds * kXcds;
-  if (need_q) {
-    hipLaunchKernelGGL(bwd_preprocess, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
-                       static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse,
-                       lse2, delta, B, Hq, Nq);
-    if (int rc = launched()) return rc;
-  }
-  if (need_k) {
-    p.nblk = (Nk + kKeysPerWg - 1) / kKeysPerWg;
-    const long grid = units8 * p.nblk;
-    if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
-    if (causal)
-      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<true>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st,
-                         p);
-    else
-      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<false>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st,
-                         p);
-    if (int rc = launched()) return rc;
-  }
-  if (need_q) {
-    p.nblk = (Nq + kDqRows - 1) / kDqRows;
-    const long grid = units8 * p.nblk * p.G;
-    if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
-    if (causal)
-      hipLaunchKernelGGL(bwd_dq_pp_kernel<true>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st, p);
-    else
-      hipLaunchKernelGGL(bwd_dq_pp_kernel<false>, dim3((unsigned)grid), dim3(kBwPpThreads), 0, st,
-                         p);
-    if (int rc = launched()) return rc;
-  }
-  return ATTN_OK;
+  return launch_backward(p, static_cast<const __bf16*>(o), lse, B, Nq, nullptr, need_q, need_k,
+                         causal != 0, st);
 }
 
+
+extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               void* workspace, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int num_seqs, int total_q, int Hq,
+                               int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                               int causal, const int32_t* seq_order, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_SIZE;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
+  if (d != kD) return ATTN_ERR_HEAD_DIM;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SIZE;
+  if (num_seqs == 0 || (max_seqlen_q == 0 && max_seqlen_k == 0)) return ATTN_OK;
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
+  const bool need_q = max_seqlen_q > 0 && total_q > 0, need_k = max_seqlen_k > 0;
+  if ((need_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) ||
+      (need_q && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+                  dq == nullptr || workspace == nullptr)))
+    return ATTN_ERR_NULL;
+  if ((need_q && (!aligned16(q) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+                  !aligned16(workspace) || (reinterpret_cast<uintptr_t>(lse) % 4) != 0)) ||
+      (need_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))))
+    return ATTN_ERR_ALIGN;
+  const long rows = (long)total_q * Hq;
+  if (rows > INT_MAX) return ATTN_ERR_TOO_LARGE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  BwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.dout = static_cast<const __bf16*>(dout);
+  float* lse2 = static_cast<float*>(workspace);
+  p.lse2 = lse2;
+  p.delta = lse2 + rows;
+  p.dq = static_cast<__bf16*>(dq);
+  p.dk = static_cast<__bf16*>(dk);
+  p.dv = static_cast<__bf16*>(dv);
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.seq_order = seq_order;
+  p.B = num_seqs;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.Nq = max_seqlen_q;
+  p.Nk = max_seqlen_k;
+  p.Tq = total_q;
+  p.scale = scale;
+  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  return launch_backward(p, static_cast<const __bf16*>(o), lse, 1, total_q,
+                         cu_seqlens_q + num_seqs, need_q, need_k, causal != 0, st);
+}

@@ -207,6 +207,36 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
              void* stream);
 
+/*
+ * Backward pass of the packed variable-length forward (attn_fwd_varlen):
+ * the same equations as attn_bwd, per sequence, with the sequences stored
+ * back to back as that forward describes (FlashAttention notes (xwysyy),
+ * code-structure overview, the "unpadded" interface).
+ *   q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
+ *   max_seqlen_k, scale, causal, seq_order : as passed to attn_fwd_varlen
+ *               (seq_order, from attn_varlen_plan or NULL, changes only the
+ *               schedule).
+ *   total_q   : rows of q, o, dout and dq (at least cu_seqlens_q[num_seqs]).
+ *   o, lse    : that forward's outputs: bf16 [total_q, Hq, d] and fp32 LSE
+ *               rows of cu_seqlens_q[num_seqs] entries per head, as it writes
+ *               them.
+ *   dout, dq  : bf16 [total_q, Hq, d]; dq rows of the sequences are written.
+ *   dk, dv    : bf16 [Tk, Hkv, d]; rows of the sequences' keys are written
+ *               (zero for keys that no query sees).  Rows outside every
+ *               sequence are not touched.
+ *   workspace : attn_bwd_workspace_size(1, Hq, total_q) bytes, as for
+ *               attn_bwd.
+ *   d         : 128.
+ * Deterministic, asynchronous on stream, allocates nothing.  Returns an
+ * attn_status as attn_bwd does (ATTN_ERR_NULL also for NULL cu_seqlens).
+ * num_seqs == 0, or both max_seqlen bounds 0, is a no-op.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
+                    int total_q, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int d,
+                    float scale, int causal, const int32_t* seq_order, void* stream);
+
 /* Bytes of workspace attn_bwd needs: two fp32 per (batch, query head, query
  * row); 0 when any argument is <= 0. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Nq);

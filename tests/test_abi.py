@@ -199,6 +199,43 @@ def test_attn_bwd_empty_problem_is_a_noop():
                 dv=None, ws=None) == attn.ATTN_OK
 
 
+def _bwd_varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                ws=FAKE, cq=FAKE, ck=FAKE, S=3, Tq=600, Hq=4, Hkv=2, mq=256, mk=256, d=128,
+                scale=0.088, causal=1, order=None):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_bwd_varlen(vp(q), vp(k), vp(v), vp(o), vp(lse), vp(do), vp(dq), vp(dk), vp(dv),
+                               vp(ws), vp(cq), vp(ck), S, Tq, Hq, Hkv, mq, mk, d, scale, causal,
+                               vp(order), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), attn.ATTN_ERR_NULL),
+    (dict(ck=None), attn.ATTN_ERR_NULL),
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(ws=None), attn.ATTN_ERR_NULL),
+    (dict(dk=None), attn.ATTN_ERR_NULL),
+    (dict(d=64), attn.ATTN_ERR_HEAD_DIM),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_HEADS),
+    (dict(S=-1), attn.ATTN_ERR_SIZE),
+    (dict(Tq=-1), attn.ATTN_ERR_SIZE),
+    (dict(mk=-1), attn.ATTN_ERR_SIZE),
+    (dict(scale=float("inf")), attn.ATTN_ERR_SIZE),
+    (dict(ws=FAKE + 8), attn.ATTN_ERR_ALIGN),
+    (dict(k=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(Tq=1 << 30), attn.ATTN_ERR_TOO_LARGE),
+])
+def test_attn_bwd_varlen_rejects_bad_arguments(kw, code):
+    assert _bwd_varlen(**kw) == code
+
+
+def test_attn_bwd_varlen_empty_problem_is_a_noop():
+    none = dict(q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+                ws=None, cq=None, ck=None)
+    assert _bwd_varlen(S=0, **none) == attn.ATTN_OK
+    assert _bwd_varlen(mq=0, mk=0, **none) == attn.ATTN_OK
+
+
 def test_attn_bwd_workspace_size():
     lib = attn.load_library()
     assert lib.attn_bwd_workspace_size(2, 4, 100) == 2 * 4 * 2 * 4 * 100

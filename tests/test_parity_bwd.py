@@ -5,7 +5,10 @@ seeded upstream gradient dO.  Small shapes are compared on every element of
 dQ, dK and dV; they span several key and query tiles, ragged tails,
 Nq != Nk, GQA groups and key padding.  At the benchmark's size one whole
 (batch, KV head) slice -- its query heads' dQ and the KV head's dK, dV -- is
-compared element by element.  Tolerances are derived in parity_util.
+compared element by element.  The packed (varlen) entry point is checked on
+small ragged batches in full (with a zero-length sequence, lq != lk, GQA and
+both masks) and, at the ragged benchmark's size, on its shortest sequence.
+Tolerances are derived in parity_util.
 """
 
 import math
@@ -101,3 +104,87 @@ def test_backward_full_size_slice():
         errs = grad_errors(to_np64(got), ref)
         print(f"[parity-bwd] {w.name} {name}: {errs}", flush=True)
         assert_grad_parity(errs, name)
+
+
+def _fwd_bwd_varlen(q, k, v, do, cq, ck, mq, mk, scale, causal, order=None):
+    qd, kd, vd, dod, cqd, ckd = (t.to(DEV) for t in (q, k, v, do, cq, ck))
+    od = None if order is None else order.to(DEV)
+    o, lse = attn.attn_fwd_varlen(qd, kd, vd, cqd, ckd, mq, mk, scale, causal, seq_order=od)
+    dq, dk, dv = attn.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cqd, ckd, mq, mk, scale, causal,
+                                      seq_order=od)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+VARLEN = [
+    # query lengths, key lengths (None: the same), Hq, Hkv, causal
+    ([1, 130, 257, 0, 64, 200], None, 4, 2, True),
+    ([1, 130, 257, 0, 64, 200], None, 4, 4, False),
+    ([64, 129, 5], [300, 17, 128], 2, 1, False),
+    ([64, 129, 5, 0], [300, 17, 128, 40], 4, 1, True),
+]
+
+
+@pytest.mark.parametrize("lq,lk,Hq,Hkv,causal", VARLEN)
+def test_backward_varlen_small_full_oracle(lq, lk, Hq, Hkv, causal):
+    d = 128
+    lq = torch.tensor(lq, dtype=torch.int32)
+    lk = lq.clone() if lk is None else torch.tensor(lk, dtype=torch.int32)
+    cq, ck = inputs.cu_from_lengths(lq), inputs.cu_from_lengths(lk)
+    Tq, Tk = int(cq[-1]), int(ck[-1])
+    seed = 9300 + Tq + 3 * Tk + Hq + int(causal)
+    q, _, _ = inputs.make_packed_qkv(Tq, 1, Hq, Hkv, d, seed, q_mult=2.0)
+    _, k, v = inputs.make_packed_qkv(1, Tk, Hq, Hkv, d, seed + 1)
+    do = inputs.make_dout(q.shape, seed + 2)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[parity-bwd] varlen lq={lq.tolist()} lk={lk.tolist()} Hq={Hq} Hkv={Hkv} "
+          f"causal={causal}", flush=True)
+    dq, dk, dv = _fwd_bwd_varlen(q, k, v, do, cq, ck, int(lq.max()), int(lk.max()), scale, causal)
+    rq, rk, rv = oracle.attention_backward_varlen(to_np64(q), to_np64(k), to_np64(v), to_np64(do),
+                                                  cq.numpy(), ck.numpy(), scale, causal, workers=8)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert_grad_parity(grad_errors(to_np64(got), ref), name)
+    # keys of a sequence with no query rows get exactly zero gradient
+    for z in range(len(lq)):
+        if int(lq[z]) == 0:
+            assert (dk[int(ck[z]):int(ck[z + 1])] == 0).all()
+            assert (dv[int(ck[z]):int(ck[z + 1])] == 0).all()
+
+
+def test_backward_varlen_plan_order_changes_nothing():
+    lq = torch.tensor([40, 700, 3, 260], dtype=torch.int32)
+    cq = inputs.cu_from_lengths(lq)
+    T = int(cq[-1])
+    q, k, v = inputs.make_packed_qkv(T, T, 4, 2, 128, 9400, q_mult=2.0)
+    do = inputs.make_dout(q.shape, 9401)
+    mx = int(lq.max())
+    order = attn.attn_varlen_plan(cq.to(DEV), cq.to(DEV), mx, mx, True).cpu()
+    a = _fwd_bwd_varlen(q, k, v, do, cq, cq, mx, mx, 0.088, True)
+    b = _fwd_bwd_varlen(q, k, v, do, cq, cq, mx, mx, 0.088, True, order)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_varlen_full_size_shortest_sequence():
+    """The ragged benchmark workload; its shortest sequence compared in full for two heads."""
+    w = inputs.WORKLOADS["varlen_causal_8seq_h32_d128"]
+    x = inputs.workload_inputs(w)
+    do = inputs.make_dout(x["q"].shape, w.seed + 77)
+    cu, mx = x["cu_seqlens_q"], x["max_seqlen"]
+    print(f"[parity-bwd] full size {w.name}", flush=True)
+    dq, dk, dv = _fwd_bwd_varlen(x["q"], x["k"], x["v"], do, cu, cu, mx, mx, w.scale, w.causal)
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    z = int(torch.argmin(x["lengths"]))
+    r0, r1 = int(cu[z]), int(cu[z + 1])
+    G = w.Hq // w.Hkv
+    for h in (0, w.Hq - 1):
+        hk = h // G
+        rq, rk, rv = oracle.attention_backward_head(
+            to_np64(x["q"][r0:r1, h]), to_np64(x["k"][r0:r1, hk]), to_np64(x["v"][r0:r1, hk]),
+            to_np64(do[r0:r1, h]), w.scale, w.causal)
+        errs = grad_errors(to_np64(dq[r0:r1, h]), rq)
+        print(f"[parity-bwd] {w.name} seq {z} (len {r1 - r0}) head {h} dq: {errs}", flush=True)
+        assert_grad_parity(errs, "dq")
+        if G == 1:  # with one query head per KV head, dK and dV of the head compare directly
+            assert_grad_parity(grad_errors(to_np64(dk[r0:r1, hk]), rk), "dk")
+            assert_grad_parity(grad_errors(to_np64(dv[r0:r1, hk]), rv), "dv")
