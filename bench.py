@@ -14,6 +14,11 @@ roofline    : the forward kernel against the dense bf16 MFMA peak of MI355X
               (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU); its
               duration is the mean of per-launch HIP events recorded on the
               launch stream inside the timed region.
+mfma_sustained: what the matrix cores sustain on this device with the
+              forward's instruction and nothing else (attn_probe_mfma), for
+              random and for zero operands, with the shader clock each ran at;
+              the chip lowers its clock under matrix-core load, so the published
+              peak is not reachable with random data.
 cpu_baseline: the CPU oracle as it stands, timed on this host on a bounded
               sample of heads of the same workload (heads are independent and
               equal in cost, so the rate is the workload's rate).
@@ -147,6 +152,42 @@ def cpu_baseline(w, x, target_s: float):
                       f"and P materialised, {workers} threads, {t_total:.1f} s wall"}
 
 
+def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
+    """Sustained bf16 matrix-core rate of this device, with and without operand bits.
+
+    attn_probe_mfma streams the forward's MFMA instruction over a full grid laid
+    out as the forward's (one 8-wave workgroup per CU) with no other work.
+    Random operands (uniform in
+    [-1, 1), as bf16) give the rate the forward's data allows; zeros give the
+    power-light bound.  The shader clock is the mean over waves of
+    s_memtime ticks / s_memrealtime ticks x 100 MHz.
+    """
+    wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator().manual_seed(seed)
+    cases = (("random", torch.rand((8, 64, 8), generator=g) * 2 - 1),
+             ("zeros", torch.zeros((8, 64, 8))))
+    out = {}
+    flop = attn.probe_flop(iters, wg)
+    for name, ops in cases:
+        ops = ops.to(torch.bfloat16).to(dev)
+        sink, clocks = attn.attn_probe_mfma(ops, iters, wg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            attn.attn_probe_mfma(ops, iters, wg, sink=sink, clocks=clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        c = clocks.cpu().to(torch.float64)
+        ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1
+        out[name] = {"tflops": round(flop / (ms * 1e-3) / 1e12, 1), "shader_clock_ghz": round(ghz, 3),
+                     "ms": round(ms, 4)}
+    out["workgroups"] = wg
+    out["iters"] = iters
+    return out
+
+
 def warm_up(step, n):
     """Runs n untimed warm-up steps; returns the first one's time in ms (cold caches), or None."""
     if n <= 0:
@@ -236,6 +277,8 @@ def main():
                          "workload, from the forward's O and LSE and a seeded dO")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the sustained matrix-core rate measurement (attn_probe_mfma)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device-to-device copies of BYTES bytes (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of the forward to bytes)")
@@ -292,6 +335,11 @@ def main():
 
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
+    probe = None
+    if not args.no_mfma_probe:
+        print("[bench] sustained matrix-core rate (attn_probe_mfma)", file=sys.stderr, flush=True)
+        probe = mfma_sustained(dev)
+        probe["forward_frac_of_random"] = round(achieved / probe["random"]["tflops"], 4)
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -319,6 +367,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5)},
+        "mfma_sustained": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

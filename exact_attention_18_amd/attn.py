@@ -32,7 +32,7 @@ ATTN_ERR_TOO_LARGE = -7
 
 EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen", "attn_varlen_plan",
            "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_size",
-           "attn_strerror", "attn_last_hip_error", "attn_version")
+           "attn_probe_mfma", "attn_strerror", "attn_last_hip_error", "attn_version")
 
 _lib = None
 
@@ -68,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_varlen.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_probe_mfma.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.attn_probe_mfma.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -393,3 +395,40 @@ def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
                                   _ptr(block_mask), int(block_mask.shape[0]), _stream_handle(dev))
     _check(rc, "attn_fwd_blocksparse")
     return out, lse
+
+
+PROBE_WAVES = 8  # waves per probe workgroup (include/attn.h, attn_probe_mfma)
+PROBE_MFMA_PER_ITER = 16
+PROBE_MFMA_FLOP = 2 * 32 * 32 * 16
+
+
+def attn_probe_mfma(operands: torch.Tensor, iters: int, workgroups: int,
+                    sink: Optional[torch.Tensor] = None,
+                    clocks: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Launch the matrix-core rate probe; returns (sink, clocks) on the device.
+
+    operands: bf16 [8, 64, 8] (4 A then 4 B operands, per lane).  FLOP per
+    launch is workgroups * 8 * iters * 16 * 32768 (probe_flop()).
+    clocks[w] = (shader-clock ticks, 100 MHz real-time ticks) of wave w's loop.
+    """
+    _need(operands, "operands", torch.bfloat16)
+    if tuple(operands.shape) != (8, 64, 8):
+        raise ValueError(f"operands must be [8, 64, 8], got {tuple(operands.shape)}")
+    dev = operands.device
+    n = workgroups * 64 * PROBE_WAVES
+    if sink is None:
+        sink = torch.empty(n, dtype=torch.float32, device=dev)
+    if clocks is None:
+        clocks = torch.empty((workgroups * PROBE_WAVES, 2), dtype=torch.int64, device=dev)
+    _need(sink, "sink", torch.float32, dev)
+    _need(clocks, "clocks", torch.int64, dev)
+    if sink.numel() < n or clocks.numel() < 2 * workgroups * PROBE_WAVES:
+        raise ValueError("sink or clocks too small for the grid")
+    rc = load_library().attn_probe_mfma(_ptr(operands), int(iters), int(workgroups), _ptr(sink),
+                                        _ptr(clocks), _stream_handle(dev))
+    _check(rc, "attn_probe_mfma")
+    return sink, clocks
+
+
+def probe_flop(iters: int, workgroups: int) -> float:
+    return float(workgroups) * PROBE_WAVES * iters * PROBE_MFMA_PER_ITER * PROBE_MFMA_FLOP

@@ -20,7 +20,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip", "mfma_probe.hip")]
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 

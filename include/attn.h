@@ -244,6 +244,35 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Nq);
 /* Static text for an attn_status code (never NULL). */
 const char* attn_strerror(int status);
 
+/*
+ * Matrix-core rate probe (a measurement aid; it computes nothing of the
+ * attention).  The roofline analysis of FlashAttention-4 (papercache
+ * summary), section 3.1.1, prices the attention tile in cycles of the matrix
+ * core; this call measures what that unit sustains on the device under a full
+ * grid, with the forward's instruction (v_mfma_f32_32x32x16_bf16) and no other
+ * work, so the forward's rate can be compared with it as well as with the
+ * published peak.  The clock drops under matrix-core load by an amount that
+ * depends on the operand bits, hence the caller-supplied operands.
+ *   operands   : device bf16 [8][64][8], 16-byte aligned: for each of 4 A and
+ *                then 4 B operands, lane l's 8 elements.
+ *   iters      : loop iterations per wave, >= 1; each issues 16 MFMAs of
+ *                32 x 32 x 16 (32768 FLOP each) into 8 accumulators.  FLOP per
+ *                launch = workgroups * 8 waves * iters * 16 * 32768.
+ *   workgroups : >= 1; 512 threads each (8 waves, two per SIMD), at most one
+ *                resident per CU, as the forward's; pass the CU count to run
+ *                every CU once.
+ *   sink       : device fp32 [workgroups * 512], written (keeps the work live).
+ *   clocks     : device uint64 [workgroups * 8][2], written: per wave the
+ *                shader-clock ticks (s_memtime) and the constant 100 MHz
+ *                real-time ticks (s_memrealtime) across its loop, whose
+ *                ratio gives the shader clock.
+ * Returns ATTN_ERR_NULL, ATTN_ERR_SIZE (iters or workgroups < 1),
+ * ATTN_ERR_ALIGN, ATTN_ERR_TOO_LARGE or ATTN_ERR_LAUNCH; asynchronous on
+ * stream like every other call.
+ */
+int attn_probe_mfma(const void* operands, int iters, int workgroups, float* sink, uint64_t* clocks,
+                    void* stream);
+
 /* hipError_t of the last failed launch on this thread (0 if none). */
 int attn_last_hip_error(void);
 

@@ -1,0 +1,33 @@
+"""GPU: the matrix-core rate probe (attn_probe_mfma) does all the work it counts.
+
+With every operand element 1.0, each 32x32x16 MFMA adds 16 to every
+accumulator element; a wave runs 2 MFMAs per accumulator per loop iteration,
+so each of its 8 x 16 accumulator registers ends at 32 * iters and every lane's
+sink value is 8 * 16 * 32 * iters, exactly representable in fp32 here.  Zero
+operands give zero.  The clocks record positive tick counts whose ratio is a
+plausible shader clock.
+"""
+
+import pytest
+import torch
+
+from exact_attention_18_amd import attn
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("value", [1.0, 0.0])
+def test_probe_does_every_mfma_it_counts(value):
+    iters, wg = 64, torch.cuda.get_device_properties(0).multi_processor_count
+    ops = torch.full((8, 64, 8), value, dtype=torch.bfloat16, device=DEV)
+    sink, clocks = attn.attn_probe_mfma(ops, iters, wg)
+    torch.cuda.synchronize()
+    expect = 8 * 16 * 32 * iters * value
+    assert sink.numel() == wg * 512
+    assert torch.equal(sink.cpu(), torch.full((wg * 512,), expect, dtype=torch.float32))
+    c = clocks.cpu().to(torch.float64)
+    assert (c > 0).all()
+    ghz = c[:, 0] / c[:, 1] * 0.1
+    assert ((ghz > 0.3) & (ghz < 3.0)).all(), (ghz.min().item(), ghz.max().item())
