@@ -61,8 +61,9 @@
 //
 // Two kernels
 // -----------
-// * d = 128: attn_fwd_pp_kernel, 8 waves / 256 query rows per workgroup in
-//   two groups of four; the two waves sharing a SIMD belong to different
+// * d = 128: attn_fwd_pp_kernel, 8 waves / 256 query rows per workgroup (of
+//   up to 8 query heads of one KV group, 256 / heads rows each) in two groups
+//   of four; the two waves sharing a SIMD belong to different
 //   groups and run half a period apart, so one feeds the matrix core (scores
 //   of tile j, then P V of tile j-1) while the other computes its softmax --
 //   the CDNA form of the ping-pong of FlashAttention-4 (papercache summary),
@@ -118,6 +119,7 @@ struct Params {
   int Hq, Hkv, G;
   int Nq, Nk;  // packed form: max_seqlen_q, max_seqlen_k
   int nqb;     // query blocks per (sequence, head)
+  int pack;    // query heads of one KV group per workgroup (1, 2, 4 or 8; 1 unless d = 128)
   int num_seqs;
   float c;  // scale * log2(e)
   const uint8_t* block_mask;  // block-sparse form: [mask_heads, nbq, nbk] of 128 x 128 blocks
@@ -144,17 +146,18 @@ struct WorkItem {
 
 __device__ __forceinline__ WorkItem decode_work(const Params& p, bool causal) {
   const int units = p.num_seqs * p.Hkv;
-  const int per_unit = p.nqb * p.G;
+  const int groups = p.G / p.pack;  // workgroups per query block of a unit
+  const int per_unit = p.nqb * groups;
   const int x = blockIdx.x % kXcds;
   const int r = blockIdx.x / kXcds;
   const int u = (r / per_unit) * kXcds + x;
   const int item = r % per_unit;
-  const int qbi = item / p.G;
+  const int qbi = item / groups;
   WorkItem w;
   w.valid = u < units;
   w.b = u / p.Hkv;
   w.hkv = u % p.Hkv;
-  w.gi = item % p.G;
+  w.gi = (item % groups) * p.pack;  // first query head of the group this workgroup takes
   w.qb = causal ? (p.nqb - 1 - qbi) : qbi;
   return w;
 }
@@ -559,7 +562,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
                     ? min(max(p.seq_order[wi.b], 0), p.num_seqs - 1)
                     : wi.b;
   const int hkv = wi.hkv, qb = wi.qb, gi = wi.gi;
-  const int h = hkv * p.G + gi;
+  // The workgroup takes P query heads of the KV group, 256 / P rows of each:
+  // chunk c holds rows (c % cph) * 32 .. +31 of head gi + c / cph.  The two
+  // waves of a SIMD (chunks 2s, 2s+1) always share their causal extent.
+  const int P = SPARSE ? 1 : p.pack;
+  const int cph = kPpWaves / P;               // 32-row chunks per head
+  const int rows_h = kRowsPerWave * cph;      // query rows per head
+  const int h = hkv * p.G + gi + chunk / cph;
 
   int q_len, nk;
   long q_row0, k_row0, lse_base, lse_hstride;
@@ -581,7 +590,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     lse_base = (long)b * p.Hq * p.Nq;
     lse_hstride = p.Nq;
   }
-  const int q0 = qb * kPpBr;
+  const int q0 = qb * rows_h;
   if (q0 >= q_len) return;  // uniform over the workgroup, before any barrier
 
   const long q_stride = (long)p.Hq * DQK;
@@ -592,7 +601,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const __bf16* kbase = p.k + k_row0 * k_stride + (long)hkv * DQK;
   const __bf16* vbase = p.v + k_row0 * v_stride + (long)hkv * DV;
 
-  const int wrow0 = q0 + chunk * kRowsPerWave;
+  const int wrow0 = q0 + (chunk % cph) * kRowsPerWave;
   const int qrow = wrow0 + l32;
   bf16x8 qf[T::KS];
 #pragma unroll
@@ -603,7 +612,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // qf ready before any tile load is in flight
   int kv_end = nk;
-  if (CAUSAL) kv_end = min(nk, min(q0 + kPpBr, q_len));
+  if (CAUSAL) kv_end = min(nk, min(q0 + rows_h, q_len));
   const int n_tiles = (kv_end + T::BC - 1) / T::BC;
 
   // Block-sparse: the key tiles whose 128-key block is set in either of this
@@ -963,6 +972,13 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(const int32_t
 
 constexpr bool use_pp(int d) { return d == 128; }
 
+// Query heads of one KV group that a ping-pong workgroup takes together (its
+// 256 rows are 256 / pack rows of each): the largest power of two up to 8
+// dividing the group size.  Under the causal mask, a workgroup's rows then
+// span fewer keys, so fewer tiles cross the diagonal; the K/V tile still
+// serves 256 rows.
+constexpr int pp_pack(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+
 template <int D, bool CAUSAL, bool VARLEN>
 int launch_one(const Params& p, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so the check below is ours
@@ -1026,9 +1042,10 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (B == 0 || Nq == 0) return ATTN_OK;
   rc = check_buffers(q, k, v, o, lse, Nk > 0);
   if (rc != ATTN_OK) return rc;
-  const int br = use_pp(d) ? kPpBr : kBr;
+  const int pack = use_pp(d) ? pp_pack(Hq / Hkv) : 1;
+  const int br = use_pp(d) ? kPpBr / pack : kBr;
   const long nqb = (Nq + br - 1) / br;
-  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv));
+  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv / pack));
   if (grid > INT_MAX || (long)B * Nq > INT_MAX || (long)B * Nk > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
   p.q = static_cast<const __bf16*>(q);
@@ -1043,6 +1060,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   p.Nq = Nq;
   p.Nk = Nk;
   p.nqb = static_cast<int>(nqb);
+  p.pack = pack;
   p.num_seqs = B;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   return dispatch(p, d, causal != 0, false, static_cast<int>(grid),
@@ -1061,8 +1079,9 @@ extern "C" int attn_fwd_dims(const void* q, const void* k, const void* v, void* 
   if (B == 0 || Nq == 0) return ATTN_OK;
   rc = check_buffers(q, k, v, o, lse, Nk > 0);
   if (rc != ATTN_OK) return rc;
-  const long nqb = (Nq + kPpBr - 1) / kPpBr;
-  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv));
+  const int pack = pp_pack(Hq / Hkv);
+  const long nqb = (Nq + kPpBr / pack - 1) / (kPpBr / pack);
+  const long grid = grid_size((long)B * Hkv, (long)nqb * (Hq / Hkv / pack));
   if (grid > INT_MAX || (long)B * Nq > INT_MAX || (long)B * Nk > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
   p.q = static_cast<const __bf16*>(q);
@@ -1077,6 +1096,7 @@ extern "C" int attn_fwd_dims(const void* q, const void* k, const void* v, void* 
   p.Nq = Nq;
   p.Nk = Nk;
   p.nqb = static_cast<int>(nqb);
+  p.pack = pack;
   p.num_seqs = B;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1125,6 +1145,7 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
   p.Nq = Nq;
   p.Nk = Nk;
   p.nqb = static_cast<int>(nqb);
+  p.pack = 1;  // the mask is per 128-row block of one head
   p.num_seqs = B;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.block_mask = block_mask;
@@ -1159,9 +1180,10 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
   rc = check_buffers(q, k, v, o, lse, max_seqlen_k > 0);
   if (rc != ATTN_OK) return rc;
-  const int br = use_pp(d) ? kPpBr : kBr;
+  const int pack = use_pp(d) ? pp_pack(Hq / Hkv) : 1;
+  const int br = use_pp(d) ? kPpBr / pack : kBr;
   const long nqb = (max_seqlen_q + br - 1) / br;
-  const long grid = grid_size((long)num_seqs * Hkv, (long)nqb * (Hq / Hkv));
+  const long grid = grid_size((long)num_seqs * Hkv, (long)nqb * (Hq / Hkv / pack));
   if (grid > INT_MAX) return ATTN_ERR_TOO_LARGE;
   Params p{};
   p.q = static_cast<const __bf16*>(q);
@@ -1178,6 +1200,7 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   p.Nq = max_seqlen_q;
   p.Nk = max_seqlen_k;
   p.nqb = static_cast<int>(nqb);
+  p.pack = pack;
   p.num_seqs = num_seqs;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   return dispatch(p, d, causal != 0, true, static_cast<int>(grid),
