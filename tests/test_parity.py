@@ -259,6 +259,48 @@ def test_reruns_are_bitwise_identical():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("B,N,Hq,Hkv,causal,padded", [
+    (2, 1000, 8, 2, True, False),    # 4 heads per workgroup
+    (1, 700, 16, 2, True, True),     # 8 heads per workgroup, key padding
+    (2, 517, 6, 3, True, False),     # 2 heads per workgroup
+    (1, 300, 12, 4, False, False),   # 1 head per workgroup (G = 3), non-causal
+])
+def test_grouped_heads_equal_repeated_kv_heads_bitwise(B, N, Hq, Hkv, causal, padded):
+    """GQA (h_kv = h_q // G) is MHA with each K/V head repeated G times.
+
+    The d = 128 kernel packs up to 8 query heads of a KV group into one
+    workgroup (256 / heads rows each) while the MHA call takes one head per
+    workgroup; a row's arithmetic does not depend on that, so the outputs are
+    bitwise equal.
+    """
+    G = Hq // Hkv
+    q, k, v = inputs.make_qkv(B, N, N, Hq, Hkv, 128, 8600 + Hq + N, q_mult=3.0)
+    seqlens = inputs.make_seqlens(B, N // 2, N, 8700 + N) if padded else None
+    kr = k.repeat_interleave(G, dim=2).contiguous()
+    vr = v.repeat_interleave(G, dim=2).contiguous()
+    print(f"[parity] gqa bitwise B={B} N={N} Hq={Hq} Hkv={Hkv} causal={causal} padded={padded}",
+          flush=True)
+    o1, l1 = _run(q, k, v, 0.088, causal, seqlens)
+    o2, l2 = _run(q, kr, vr, 0.088, causal, seqlens)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_grouped_heads_equal_repeated_kv_heads_bitwise_varlen():
+    lengths = torch.tensor([300, 1, 517, 0, 256], dtype=torch.int32)
+    cu = inputs.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    q, k, v = inputs.make_packed_qkv(T, T, 8, 2, 128, 8800, q_mult=3.0)
+    mx = int(lengths.max())
+    outs = []
+    for kk, vv in ((k, v), (k.repeat_interleave(4, dim=1).contiguous(),
+                            v.repeat_interleave(4, dim=1).contiguous())):
+        o, lse = attn.attn_fwd_varlen(q.to(DEV), kk.to(DEV), vv.to(DEV), cu.to(DEV), cu.to(DEV),
+                                      mx, mx, 0.088, True)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_key_shift_moves_lse_by_the_query_dot_shift():
     """softmax(x) = softmax(x - c): adding w to every key moves LSE_i by scale*q_i.w."""
     B, N, H, d = 1, 300, 2, 64
