@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   for (int dt = 0; dt < T::DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY;  // running max, log2 domain (scores times scale*log2 e)
   float l_run = 0.f;        // this lane's half of the running sum
+  float m_use = 0.f;        // m_run, or 0 while it is -inf (no visible key yet)
   float alpha = 1.f;
   bool rescale_o = false;   // wave-uniform: O must be multiplied by alpha
 
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     const bool do_sm = FAST || active(j);
     const bool do_s = FAST || (j + 1 < n_tiles && active(j + 1));
     if (!FAST && do_sm && needs_mask(j)) apply_mask(j);
-    float m0 = -INFINITY, m1 = -INFINITY, m_use = 0.f;
+    float m0 = -INFINITY, m1 = -INFINITY;
     float ls[2] = {0.f, 0.f};
     // LDS operands are read kAhead slices before their MFMA.
     bf16x8 opnd[kAhead];
@@ -408,15 +409,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
             m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
           }
         } else if (sl == kDecide) {
-          // Conditional rescale (tau), decided for the whole wave.
+          // Conditional rescale (tau), decided for the whole wave; without
+          // it alpha would be exactly 1, so nothing is computed.
           const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
-          const bool any = __builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0;
-          const float m_new = any ? fmaxf(m_run, mx) : m_run;
-          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-          m_use = (m_new == -INFINITY) ? 0.f : m_new;
-          rescale_o = rescale_o || any;
+          if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            rescale_o = true;
+          }
         } else if (sl < kPv) {
           // exponentials of key block 0 over slices kDecide+1 .. kPv-1
           constexpr int nsl = kPv - kDecide - 1;
@@ -723,6 +726,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.f;
+  float m_use = 0.f;
 
   // ---- MFMA phase: S_j = K_j Q^T (key blocks interleaved), then O += P_{j-1} V_{j-1}.
   constexpr int kS = T::KT * T::KS;
@@ -796,11 +800,18 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
     }
     const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
-    const bool any = __builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0;
-    const float m_new = any ? fmaxf(m_run, mx) : m_run;
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    // The rescale (new max, alpha, l and O scaled) runs only when some row's
+    // max grew by more than tau; the test is wave-uniform, and otherwise
+    // alpha would be exactly 1.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
+    }
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kt = 0; kt < T::KT; ++kt)
@@ -816,11 +827,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         pv_op[kt][r >> 3][(r & 7) >> 1] = u;
       }
     asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
-    l_run = l_run * alpha + (ls0 + ls1);
-    if (any) {
-#pragma unroll
-      for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
-    }
+    l_run += ls0 + ls1;
   };
 
   // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
