@@ -18,7 +18,8 @@ mfma_sustained: what the matrix cores sustain on this device with the
               forward's instruction and nothing else (attn_probe_mfma), for
               random and for zero operands, with the shader clock each ran at;
               the chip lowers its clock under matrix-core load, so the published
-              peak is not reachable with random data.
+              peak is not reachable with random data.  shape_16x16x32 holds the
+              same for the 16x16x32 MFMA, which the chip runs at a higher clock.
 cpu_baseline: the CPU oracle as it stands, timed on this host on a bounded
               sample of heads of the same workload (heads are independent and
               equal in cost, so the rate is the workload's rate).
@@ -155,34 +156,41 @@ def cpu_baseline(w, x, target_s: float):
 def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
     """Sustained bf16 matrix-core rate of this device, with and without operand bits.
 
-    attn_probe_mfma streams the forward's MFMA instruction over a full grid laid
-    out as the forward's (one 8-wave workgroup per CU) with no other work.
-    Random operands (uniform in
-    [-1, 1), as bf16) give the rate the forward's data allows; zeros give the
-    power-light bound.  The shader clock is the mean over waves of
-    s_memtime ticks / s_memrealtime ticks x 100 MHz.
+    attn_probe_mfma streams one MFMA shape over a full grid laid out as the
+    forward's (one 8-wave workgroup per CU) with no other work: the forward's
+    32x32x16 (the "random" and "zeros" entries) and, for comparison, 16x16x32
+    (the "shape_16x16x32" entry).  Random operands (uniform in [-1, 1), as
+    bf16) give the rate the forward's data allows; zeros give the power-light
+    bound.  The shader clock is the mean over waves of s_memtime ticks /
+    s_memrealtime ticks x 100 MHz.
     """
     wg = torch.cuda.get_device_properties(dev).multi_processor_count
     g = torch.Generator().manual_seed(seed)
     cases = (("random", torch.rand((8, 64, 8), generator=g) * 2 - 1),
              ("zeros", torch.zeros((8, 64, 8))))
-    out = {}
     flop = attn.probe_flop(iters, wg)
-    for name, ops in cases:
-        ops = ops.to(torch.bfloat16).to(dev)
-        sink, clocks = attn.attn_probe_mfma(ops, iters, wg)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            attn.attn_probe_mfma(ops, iters, wg, sink=sink, clocks=clocks)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        c = clocks.cpu().to(torch.float64)
-        ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1
-        out[name] = {"tflops": round(flop / (ms * 1e-3) / 1e12, 1), "shader_clock_ghz": round(ghz, 3),
-                     "ms": round(ms, 4)}
+
+    def measure(shape):
+        res = {}
+        for name, ops in cases:
+            ops = ops.to(torch.bfloat16).to(dev)
+            sink, clocks = attn.attn_probe_mfma(ops, iters, wg, shape=shape)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                attn.attn_probe_mfma(ops, iters, wg, sink=sink, clocks=clocks, shape=shape)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            c = clocks.cpu().to(torch.float64)
+            ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1
+            res[name] = {"tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                         "shader_clock_ghz": round(ghz, 3), "ms": round(ms, 4)}
+        return res
+
+    out = measure(32)
+    out["shape_16x16x32"] = measure(16)
     out["workgroups"] = wg
     out["iters"] = iters
     return out

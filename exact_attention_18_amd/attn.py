@@ -68,7 +68,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_varlen.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.attn_probe_mfma.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.attn_probe_mfma.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.attn_probe_mfma.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -398,17 +398,18 @@ def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
 
 
 PROBE_WAVES = 8  # waves per probe workgroup (include/attn.h, attn_probe_mfma)
-PROBE_MFMA_PER_ITER = 16
-PROBE_MFMA_FLOP = 2 * 32 * 32 * 16
+PROBE_FLOP_PER_ITER = 16 * 2 * 32 * 32 * 16  # per wave, either shape
 
 
 def attn_probe_mfma(operands: torch.Tensor, iters: int, workgroups: int,
                     sink: Optional[torch.Tensor] = None,
-                    clocks: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    clocks: Optional[torch.Tensor] = None,
+                    shape: int = 32) -> Tuple[torch.Tensor, torch.Tensor]:
     """Launch the matrix-core rate probe; returns (sink, clocks) on the device.
 
-    operands: bf16 [8, 64, 8] (4 A then 4 B operands, per lane).  FLOP per
-    launch is workgroups * 8 * iters * 16 * 32768 (probe_flop()).
+    operands: bf16 [8, 64, 8] (4 A then 4 B operands, per lane).  shape: 32
+    (the forward's 32x32x16 MFMA) or 16 (16x16x32).  FLOP per launch is
+    workgroups * 8 * iters * 16 * 32768 for either shape (probe_flop()).
     clocks[w] = (shader-clock ticks, 100 MHz real-time ticks) of wave w's loop.
     """
     _need(operands, "operands", torch.bfloat16)
@@ -424,11 +425,11 @@ def attn_probe_mfma(operands: torch.Tensor, iters: int, workgroups: int,
     _need(clocks, "clocks", torch.int64, dev)
     if sink.numel() < n or clocks.numel() < 2 * workgroups * PROBE_WAVES:
         raise ValueError("sink or clocks too small for the grid")
-    rc = load_library().attn_probe_mfma(_ptr(operands), int(iters), int(workgroups), _ptr(sink),
-                                        _ptr(clocks), _stream_handle(dev))
+    rc = load_library().attn_probe_mfma(_ptr(operands), int(shape), int(iters), int(workgroups),
+                                        _ptr(sink), _ptr(clocks), _stream_handle(dev))
     _check(rc, "attn_probe_mfma")
     return sink, clocks
 
 
 def probe_flop(iters: int, workgroups: int) -> float:
-    return float(workgroups) * PROBE_WAVES * iters * PROBE_MFMA_PER_ITER * PROBE_MFMA_FLOP
+    return float(workgroups) * PROBE_WAVES * iters * PROBE_FLOP_PER_ITER

@@ -35,11 +35,11 @@
 //   order (the determinism concern of FlashAttention-4 (papercache summary),
 //   section 3.2.4).
 //
-// LDS tiles hold rows of d = 128 bf16 padded to a pitch of 152 elements
-// (304 bytes): a 16-lane row read and a 32-lane transpose read then touch
-// distinct or at most doubly used banks, and every read is one per-lane base
-// address plus a compile-time offset, which keeps the kernels' address
-// registers few.
+// LDS tiles hold rows of d = 128 bf16 in groups of 16 rows, each row starting
+// at a staggered 16-byte unit of its group (the layout is described at
+// row_slot below): 16-lane row reads and transpose reads meet no bank twice,
+// and every read is one per-lane base address plus a compile-time offset,
+// which keeps the kernels' address registers few.
 
 #include <hip/hip_runtime.h>
 

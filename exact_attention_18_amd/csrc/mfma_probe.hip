@@ -1,5 +1,6 @@
 // Sustained bf16 matrix-core rate of the device, measured with the forward's
-// own instruction (v_mfma_f32_32x32x16_bf16) and nothing else.
+// own instruction (v_mfma_f32_32x32x16_bf16), or the 16x16x32 shape, and
+// nothing else.
 //
 // The roofline analysis of "FlashAttention-4: Algorithm and Kernel Pipelining
 // Co-Design for Asymmetric Hardware Scaling" (papercache summary), section
@@ -12,13 +13,16 @@
 // caller (random data for the rate the forward can meet, zeros for the
 // power-light bound) and reports the shader clock it ran at.
 //
-// Each wave holds four A and four B operands in VGPRs and issues 16 MFMAs per
-// loop iteration into eight independent accumulators, every MFMA on a
-// different (A, B) pair from the one before, so consecutive instructions change
-// both operands.  The launch mirrors the forward's: one workgroup of 8 waves
-// per CU, two waves per SIMD (the accumulators take enough registers that a
-// second workgroup does not fit on a CU).  With more waves per SIMD the matrix
-// core was measured to sustain less, not more.
+// Each wave holds four A and four B operands in VGPRs and issues MFMAs into
+// independent accumulators, every MFMA on a different (A, B) pair from the
+// one before, so consecutive instructions change both operands.  Two shapes:
+// the forward's 32x32x16 (16 MFMAs per loop iteration, 8 accumulators) and
+// 16x16x32 (32 MFMAs of half the FLOPs, 16 accumulators), the same FLOPs per
+// iteration.  The launch mirrors the forward's: one workgroup of 8 waves per
+// CU, two waves per SIMD; each workgroup reserves more than half of the CU's
+// LDS, so a second one never shares its CU whatever the register count.
+// With more waves per SIMD the matrix core was measured to sustain less, not
+// more.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -28,15 +32,18 @@
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kProbeWaves = 8;
 constexpr int kProbeThreads = 64 * kProbeWaves;
-constexpr int kProbeMfmaPerIter = 16;
-constexpr int kProbeAcc = 8;
+constexpr int kProbeLdsFloats = 84 * 1024 / 4;  // 84 KB of the CU's 160 KB
 
+template <int SHAPE>
 __global__ __launch_bounds__(kProbeThreads, 1) void mfma_probe_kernel(const bf16x8* __restrict__ ops,
                                                                        int iters,
                                                                        float* __restrict__ sink,
                                                                        uint64_t* __restrict__ clocks) {
+  __shared__ float reserve[kProbeLdsFloats];
   const int lane = threadIdx.x & 63;
   bf16x8 a[4], b[4];
 #pragma unroll
@@ -44,29 +51,55 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_probe_kernel(const bf16
     a[i] = ops[i * 64 + lane];
     b[i] = ops[(4 + i) * 64 + lane];
   }
-  f32x16 acc[kProbeAcc];
-#pragma unroll
-  for (int i = 0; i < kProbeAcc; ++i) acc[i] = f32x16{};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     asm volatile("" : "+v"(a[i]), "+v"(b[i]));  // operands in place before the clock starts
-  const uint64_t t0 = __builtin_amdgcn_s_memtime();
-  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-  for (int it = 0; it < iters; ++it) {
-    // MFMA k: accumulator k % 8, A operand k % 4, B operand (k + k / 4) % 4
-    static_for<0, kProbeMfmaPerIter>([&](auto I) __attribute__((always_inline)) {
-      constexpr int k = decltype(I)::value;
-      acc[k % kProbeAcc] = mfma32(a[k % 4], b[(k + k / 4) % 4], acc[k % kProbeAcc]);
-    });
-  }
-  const uint64_t t1 = __builtin_amdgcn_s_memtime();
-  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
   float s = 0.f;
+  uint64_t t0, r0, t1, r1;
+  if constexpr (SHAPE == 32) {
+    f32x16 acc[8];
 #pragma unroll
-  for (int i = 0; i < kProbeAcc; ++i)
+    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+      // MFMA k: accumulator k % 8, A operand k % 4, B operand (k + k / 4) % 4
+      static_for<0, 16>([&](auto I) __attribute__((always_inline)) {
+        constexpr int k = decltype(I)::value;
+        acc[k % 8] = mfma32(a[k % 4], b[(k + k / 4) % 4], acc[k % 8]);
+      });
+    }
+    t1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += acc[i][e];
-  sink[(long)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += acc[i][e];
+  } else {
+    f32x4 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = f32x4{};
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+      // MFMA k: accumulator k % 16, A operand k % 4, B operand (k + k / 4) % 4
+      static_for<0, 32>([&](auto I) __attribute__((always_inline)) {
+        constexpr int k = decltype(I)::value;
+        acc[k % 16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k % 4], b[(k + k / 4) % 4],
+                                                              acc[k % 16], 0, 0, 0);
+      });
+    }
+    t1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += acc[i][e];
+  }
+  // The sum passes through the reserved LDS so that the reservation stays.
+  volatile float* res = reserve;
+  res[threadIdx.x] = s;
+  sink[(long)blockIdx.x * kProbeThreads + threadIdx.x] = res[threadIdx.x];
   if (lane == 0) {
     const long w = (long)blockIdx.x * kProbeWaves + (threadIdx.x >> 6);
     clocks[2 * w] = t1 - t0;
@@ -76,17 +109,23 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_probe_kernel(const bf16
 
 }  // namespace
 
-extern "C" int attn_probe_mfma(const void* operands, int iters, int workgroups, float* sink,
-                               uint64_t* clocks, void* stream) {
+extern "C" int attn_probe_mfma(const void* operands, int shape, int iters, int workgroups,
+                               float* sink, uint64_t* clocks, void* stream) {
   if (operands == nullptr || sink == nullptr || clocks == nullptr) return ATTN_ERR_NULL;
-  if (iters < 1 || workgroups < 1) return ATTN_ERR_SIZE;
+  if ((shape != 32 && shape != 16) || iters < 1 || workgroups < 1) return ATTN_ERR_SIZE;
   if ((reinterpret_cast<uintptr_t>(operands) & 15u) != 0 ||
       (reinterpret_cast<uintptr_t>(sink) & 3u) != 0 || (reinterpret_cast<uintptr_t>(clocks) & 7u) != 0)
     return ATTN_ERR_ALIGN;
   if (workgroups > (INT32_MAX / kProbeThreads)) return ATTN_ERR_TOO_LARGE;
-  hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(kProbeThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const bf16x8*>(operands), iters,
-                     sink, clocks);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  const auto* ops = static_cast<const bf16x8*>(operands);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (shape == 32)
+    hipLaunchKernelGGL(mfma_probe_kernel<32>, dim3(workgroups), dim3(kProbeThreads), 0, st, ops,
+                       iters, sink, clocks);
+  else
+    hipLaunchKernelGGL(mfma_probe_kernel<16>, dim3(workgroups), dim3(kProbeThreads), 0, st, ops,
+                       iters, sink, clocks);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) {
     attn_detail::last_hip_error = static_cast<int>(err);

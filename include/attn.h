@@ -249,29 +249,34 @@ const char* attn_strerror(int status);
  * attention).  The roofline analysis of FlashAttention-4 (papercache
  * summary), section 3.1.1, prices the attention tile in cycles of the matrix
  * core; this call measures what that unit sustains on the device under a full
- * grid, with the forward's instruction (v_mfma_f32_32x32x16_bf16) and no other
- * work, so the forward's rate can be compared with it as well as with the
- * published peak.  The clock drops under matrix-core load by an amount that
- * depends on the operand bits, hence the caller-supplied operands.
+ * grid, with the forward's instruction (v_mfma_f32_32x32x16_bf16) or the
+ * 16x16x32 shape and no other work, so the forward's rate can be compared
+ * with it as well as with the published peak.  The clock drops under
+ * matrix-core load by an amount that depends on the operand bits, hence the
+ * caller-supplied operands.
  *   operands   : device bf16 [8][64][8], 16-byte aligned: for each of 4 A and
  *                then 4 B operands, lane l's 8 elements.
- *   iters      : loop iterations per wave, >= 1; each issues 16 MFMAs of
- *                32 x 32 x 16 (32768 FLOP each) into 8 accumulators.  FLOP per
- *                launch = workgroups * 8 waves * iters * 16 * 32768.
- *   workgroups : >= 1; 512 threads each (8 waves, two per SIMD), at most one
- *                resident per CU, as the forward's; pass the CU count to run
- *                every CU once.
+ *   shape      : 32 (v_mfma_f32_32x32x16_bf16: 16 MFMAs per iteration into
+ *                8 accumulators) or 16 (v_mfma_f32_16x16x32_bf16: 32 MFMAs
+ *                per iteration into 16 accumulators); either way 16 * 32768
+ *                FLOP per wave and iteration.
+ *   iters      : loop iterations per wave, >= 1.  FLOP per launch =
+ *                workgroups * 8 waves * iters * 16 * 32768.
+ *   workgroups : >= 1; 512 threads each (8 waves, two per SIMD), one resident
+ *                per CU (each reserves 84 KB of LDS), as the forward's; pass
+ *                the CU count to run every CU once.
  *   sink       : device fp32 [workgroups * 512], written (keeps the work live).
+ *                With every operand element 1.0 each value is 4096 * iters.
  *   clocks     : device uint64 [workgroups * 8][2], written: per wave the
  *                shader-clock ticks (s_memtime) and the constant 100 MHz
  *                real-time ticks (s_memrealtime) across its loop, whose
  *                ratio gives the shader clock.
- * Returns ATTN_ERR_NULL, ATTN_ERR_SIZE (iters or workgroups < 1),
- * ATTN_ERR_ALIGN, ATTN_ERR_TOO_LARGE or ATTN_ERR_LAUNCH; asynchronous on
- * stream like every other call.
+ * Returns ATTN_ERR_NULL, ATTN_ERR_SIZE (shape not 32 or 16, iters or
+ * workgroups < 1), ATTN_ERR_ALIGN, ATTN_ERR_TOO_LARGE or ATTN_ERR_LAUNCH;
+ * asynchronous on stream like every other call.
  */
-int attn_probe_mfma(const void* operands, int iters, int workgroups, float* sink, uint64_t* clocks,
-                    void* stream);
+int attn_probe_mfma(const void* operands, int shape, int iters, int workgroups, float* sink,
+                    uint64_t* clocks, void* stream);
 
 /* hipError_t of the last failed launch on this thread (0 if none). */
 int attn_last_hip_error(void);

@@ -302,10 +302,10 @@ def test_attn_fwd_blocksparse_empty_is_a_noop():
     assert _bsp(B=0, q=None, k=None, v=None, o=None, lse=None, mask=None) == attn.ATTN_OK
 
 
-def _probe(ops=FAKE, iters=16, wg=2, sink=FAKE, clocks=FAKE):
+def _probe(ops=FAKE, shape=32, iters=16, wg=2, sink=FAKE, clocks=FAKE):
     lib = attn.load_library()
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.attn_probe_mfma(vp(ops), iters, wg, vp(sink), vp(clocks), None)
+    return lib.attn_probe_mfma(vp(ops), shape, iters, wg, vp(sink), vp(clocks), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -314,6 +314,8 @@ def _probe(ops=FAKE, iters=16, wg=2, sink=FAKE, clocks=FAKE):
     (dict(clocks=None), attn.ATTN_ERR_NULL),
     (dict(iters=0), attn.ATTN_ERR_SIZE),
     (dict(wg=0), attn.ATTN_ERR_SIZE),
+    (dict(shape=64), attn.ATTN_ERR_SIZE),
+    (dict(shape=0), attn.ATTN_ERR_SIZE),
     (dict(ops=FAKE + 8), attn.ATTN_ERR_ALIGN),
     (dict(clocks=FAKE + 4), attn.ATTN_ERR_ALIGN),
     (dict(wg=1 << 30), attn.ATTN_ERR_TOO_LARGE),

@@ -3,8 +3,9 @@
 With every operand element 1.0, each 32x32x16 MFMA adds 16 to every
 accumulator element; a wave runs 2 MFMAs per accumulator per loop iteration,
 so each of its 8 x 16 accumulator registers ends at 32 * iters and every lane's
-sink value is 8 * 16 * 32 * iters, exactly representable in fp32 here.  Zero
-operands give zero.  The clocks record positive tick counts whose ratio is a
+sink value is 8 * 16 * 32 * iters, exactly representable in fp32 here.  The
+16x16x32 shape adds 32 per MFMA into 16 x 4 registers, 2 MFMAs each per
+iteration: the same 4096 * iters.  Zero operands give zero.  The clocks record positive tick counts whose ratio is a
 plausible shader clock.
 """
 
@@ -18,13 +19,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
+@pytest.mark.parametrize("shape", [32, 16])
 @pytest.mark.parametrize("value", [1.0, 0.0])
-def test_probe_does_every_mfma_it_counts(value):
+def test_probe_does_every_mfma_it_counts(value, shape):
     iters, wg = 64, torch.cuda.get_device_properties(0).multi_processor_count
     ops = torch.full((8, 64, 8), value, dtype=torch.bfloat16, device=DEV)
-    sink, clocks = attn.attn_probe_mfma(ops, iters, wg)
+    sink, clocks = attn.attn_probe_mfma(ops, iters, wg, shape=shape)
     torch.cuda.synchronize()
-    expect = 8 * 16 * 32 * iters * value
+    expect = 4096 * iters * value
     assert sink.numel() == wg * 512
     assert torch.equal(sink.cpu(), torch.full((wg * 512,), expect, dtype=torch.float32))
     c = clocks.cpu().to(torch.float64)
