@@ -213,8 +213,8 @@ def warm_up(step, n):
 
 def bench_backward(args, w, x, dev, fwd_flops):
     """Times attn_bwd on the workload (FLOPs: 2.5x the forward, as the pages count them)."""
-    if w.sparse or w.d != 128 or w.d_v != 128:
-        print("the backward covers the dense d=128 workloads", file=sys.stderr)
+    if w.sparse or w.d not in (64, 128) or w.d_v != w.d:
+        print("the backward covers the dense workloads with d = 64 or 128", file=sys.stderr)
         sys.exit(2)
     q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
     do = inputs.make_dout(x["q"].shape, w.seed + 77).to(dev)
@@ -258,7 +258,7 @@ def bench_backward(args, w, x, dev, fwd_flops):
     # dQ kernel's three (S and dP are formed in both), i.e. 3.5x the forward's two.
     issued = 3.5 * fwd_flops / (ms * 1e-3) / 1e12
     line = {
-        "metric": "attn bwd TFLOP/s bf16 hd128 (2.5x forward FLOPs)",
+        "metric": f"attn bwd TFLOP/s bf16 hd{w.d} (2.5x forward FLOPs)",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "first_run_ms": first_ms,
         "higher_is_better": True,

@@ -250,7 +250,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV (bf16) of the batched forward from its O and LSE and the upstream dO.
 
-    Layouts as in attn_fwd; d must be 128.  The workspace (uint8, at least
+    Layouts as in attn_fwd; d is 64 or 128.  The workspace (uint8, at least
     attn_bwd_workspace_size bytes) is allocated here when not given.
     """
     lib = load_library()
@@ -307,7 +307,7 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     """dQ, dK, dV (bf16) of the packed forward (attn_fwd_varlen) from its O and LSE.
 
     q, o, dout [Tq,Hq,d]; k, v [Tk,Hkv,d]; lse [Hq,Tq] as attn_fwd_varlen
-    returns it; d must be 128.  Rows and keys that belong to no sequence are
+    returns it; d is 64 or 128.  Rows and keys that belong to no sequence are
     not written (zero when dq, dk, dv are allocated here).
     """
     lib = load_library()

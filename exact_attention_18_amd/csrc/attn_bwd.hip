@@ -35,7 +35,8 @@
 //   order (the determinism concern of FlashAttention-4 (papercache summary),
 //   section 3.2.4).
 //
-// LDS tiles hold rows of d = 128 bf16 in groups of 16 rows, each row starting
+// Head dimensions 64 and 128 (template parameter D of every kernel).  LDS
+// tiles hold rows of D bf16 in groups of 16 rows, each row starting
 // at a staggered 16-byte unit of its group (the layout is described at
 // row_slot below): 16-lane row reads and transpose reads meet no bank twice,
 // and every read is one per-lane base address plus a compile-time offset,
@@ -53,8 +54,7 @@
 
 namespace {
 
-constexpr int kD = 128;                 // head dimension of the backward kernels
-constexpr int kChunks = kD / 8;         // 16-byte chunks per row
+// Head dimensions D of the backward kernels: 64 and 128.
 constexpr int kBwThreads = 256;         // 4 waves
 constexpr int kKeysPerWg = 128;         // dK/dV kernel: keys per workgroup
 constexpr int kQStep = 32;              // dK/dV kernel: query rows per step
@@ -125,40 +125,45 @@ __device__ __forceinline__ UnitRows unit_rows(const BwdParams& p, int b) {
   return r;
 }
 
-// LDS tile layout.  Rows (d = 128 bf16, 256 bytes) come in groups of 16; a
-// group spans 272 16-byte units and its row r starts at unit 17 a(r), with
-// a(r) = 4 (r % 4) + r / 4.  Since 17 a(r) = a(r) (mod 16), a 16-lane row
+// LDS tile layout.  Rows (D bf16, D/8 16-byte units) come in groups of 16; a
+// group spans 16 (D/8 + 1) units and its row r starts at unit (D/8 + 1) a(r),
+// with a(r) = 4 (r % 4) + r / 4.  D/8 + 1 (17 or 9) is odd, so a 16-lane row
 // read (rows r0..r0+15, one chunk) meets 16 distinct 16-byte bank groups, and
 // a transpose read (rows r0 + 4g + m, m = 0..3, 64 contiguous bytes each)
-// meets 4 (r % 4) + const, four disjoint 64-byte bank ranges: neither
+// starts at 4 (D/8 + 1) m + const, four disjoint 64-byte bank ranges: neither
 // conflicts.  Rows are contiguous, so every read is one per-lane base address
 // plus a compile-time offset.
-constexpr int kGroupElems = 16 * 17 * 8;   // elements per group of 16 rows
-constexpr int kRowElems = kGroupElems / 16;  // tile size per row (tiles hold multiples of 16 rows)
+template <int D>
+struct Lds {
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int kStride = kChunks + 1;             // units per row slot
+  static constexpr int kGroupElems = 16 * kStride * 8;    // elements per group of 16 rows
+  static constexpr int kRowElems = kGroupElems / 16;      // tile size per row (multiples of 16 rows)
 
-// 16-byte unit at which row r (0..15) of a group starts.
-__device__ __forceinline__ int row_slot(int r) { return 17 * (4 * (r & 3) + (r >> 2)); }
+  // 16-byte unit at which row r (0..15) of a group starts.
+  static __device__ __forceinline__ int row_slot(int r) { return kStride * (4 * (r & 3) + (r >> 2)); }
 
-// Element offset of (row, 16-byte chunk) in a tile.
-__device__ __forceinline__ int tile_off(int row, int chunk) {
-  return kGroupElems * (row >> 4) + 8 * (row_slot(row & 15) + chunk);
-}
+  // Element offset of (row, 16-byte chunk) in a tile.
+  static __device__ __forceinline__ int tile_off(int row, int chunk) {
+    return kGroupElems * (row >> 4) + 8 * (row_slot(row & 15) + chunk);
+  }
 
-// Row-operand read: lane l takes row r0 + l%32, elements 16*ks + 8*(l/32) .. +7
-// (r0 a multiple of 16).
-__device__ __forceinline__ bf16x8 read_rows(const __bf16* t, int r0, int ks, int lane) {
-  const int lane_off = kGroupElems * ((lane >> 4) & 1) + 8 * (row_slot(lane & 15) + (lane >> 5));
-  return *reinterpret_cast<const bf16x8*>(t + kGroupElems * (r0 >> 4) + lane_off + 16 * ks);
-}
+  // Row-operand read: lane l takes row r0 + l%32, elements 16*ks + 8*(l/32) .. +7
+  // (r0 a multiple of 16).
+  static __device__ __forceinline__ bf16x8 read_rows(const __bf16* t, int r0, int ks, int lane) {
+    const int lane_off = kGroupElems * ((lane >> 4) & 1) + 8 * (row_slot(lane & 15) + (lane >> 5));
+    return *reinterpret_cast<const bf16x8*>(t + kGroupElems * (r0 >> 4) + lane_off + 16 * ks);
+  }
 
-// Transposed operand: rows r0 + {4g..4g+3} then r0 + {8+4g..8+4g+3} (g = lane/32), as the
-// k-elements, for column d0 + lane%32 of the operand (r0 a multiple of 16, d0 of 32).
-__device__ __forceinline__ bf16x8 read_cols(const __bf16* t, int r0, int d0, int lane) {
-  const int g = lane >> 5, m = (lane & 15) >> 2, u = lane & 3;
-  // first of this lane's 4 columns: d0 + 16 ((lane/16) % 2) + 4u
-  const __bf16* base = t + kGroupElems * (r0 >> 4) + d0 + 16 * ((lane >> 4) & 1) + 4 * u;
-  return read_tr_pair(base + 8 * row_slot(4 * g + m), base + 8 * row_slot(8 + 4 * g + m));
-}
+  // Transposed operand: rows r0 + {4g..4g+3} then r0 + {8+4g..8+4g+3} (g = lane/32), as the
+  // k-elements, for column d0 + lane%32 of the operand (r0 a multiple of 16, d0 of 32).
+  static __device__ __forceinline__ bf16x8 read_cols(const __bf16* t, int r0, int d0, int lane) {
+    const int g = lane >> 5, m = (lane & 15) >> 2, u = lane & 3;
+    // first of this lane's 4 columns: d0 + 16 ((lane/16) % 2) + 4u
+    const __bf16* base = t + kGroupElems * (r0 >> 4) + d0 + 16 * ((lane >> 4) & 1) + 4 * u;
+    return read_tr_pair(base + 8 * row_slot(4 * g + m), base + 8 * row_slot(8 + 4 * g + m));
+  }
+};
 
 // Buffer descriptor over [base, base + bytes), both uniform over the wave.
 // readfirstlane keeps them in scalar registers: a descriptor the compiler
@@ -174,8 +179,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 
 // Global rows [row0, row0 + rows) of a [.., stride] bf16 array -> padded LDS tile.
 // Loads are 16 bytes per lane, row-contiguous; rows >= valid read as zero.
-template <int ROWS>
+template <int ROWS, int D>
 struct TileCopy {
+  static constexpr int kChunks = D / 8;
   static constexpr int kPer = ROWS * kChunks / kBwThreads;  // chunks per thread
   static_assert(kPer * kBwThreads == ROWS * kChunks, "tile split");
   u32x4 r[kPer];
@@ -193,32 +199,35 @@ struct TileCopy {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + i * kBwThreads;
-      *reinterpret_cast<u32x4*>(tile + tile_off(c / kChunks, c % kChunks)) = r[i];
+      *reinterpret_cast<u32x4*>(tile + Lds<D>::tile_off(c / kChunks, c % kChunks)) = r[i];
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// D = <dO, O> and LSE in log2 units, one row per 16 lanes.
+// D = <dO, O> and LSE in log2 units, one row per D/8 lanes.
 // Packed form (B = 1, Nq = total rows): lse_rows points at the forward's LSE
 // row count per head (cu_seqlens_q[num_seqs]); rows past it belong to no
 // sequence and are skipped.  Batched form: lse_rows is null.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess(const __bf16* o, const __bf16* dout,
                                                       const float* lse, float* lse2, float* delta,
                                                       int B, int Hq, int Nq,
                                                       const int32_t* lse_rows) {
+  constexpr int kLanes = D / 8;            // lanes per row
+  constexpr int kRows = 256 / kLanes;      // rows per block
   const long rows = (long)B * Nq * Hq;
-  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);  // row of [B, Nq, Hq]
-  const int sub = threadIdx.x & 15;
+  const long row = (long)blockIdx.x * kRows + (threadIdx.x / kLanes);  // row of [B, Nq, Hq]
+  const int sub = threadIdx.x % kLanes;
   float acc = 0.f;
   if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * kD + sub * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * kD + sub * 8);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * D + sub * 8);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * D + sub * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
   }
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  for (int off = kLanes / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kLanes);
   if (row < rows && sub == 0) {
     const int h = (int)(row % Hq);
     const long bi = row / Hq;
@@ -251,8 +260,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const __bf16* o, const __b
 // LDS in a fixed order.
 constexpr int kBwPpThreads = 512;
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams p) {
+  using L = Lds<D>;
+  constexpr int kRowElems = L::kRowElems;
+  constexpr int TD = D / 32;  // 32-wide d blocks of dK^T, dV^T
   __shared__ __attribute__((aligned(1024))) __bf16 kv_t[2 * kKeysPerWg * kRowElems];  // K, then V
   __shared__ __attribute__((aligned(1024))) __bf16 q_t[2][2][kQStep * kRowElems];  // [group][buffer]
   __shared__ __attribute__((aligned(1024))) __bf16 do_t[2][2][kQStep * kRowElems];
@@ -277,8 +289,8 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   const int nk = ur.nk, nq = ur.nq;
   const int k0 = kb * kKeysPerWg;
   if (k0 >= ur.k_write) return;  // a packed sequence shorter than the longest; uniform
-  const long kv_stride = (long)p.Hkv * kD;
-  const long q_stride = (long)p.Hq * kD;
+  const long kv_stride = (long)p.Hkv * D;
+  const long q_stride = (long)p.Hq * D;
 
   // every tile buffer starts finite (periods without a step multiply zeros by
   // it); the barrier orders these stores before the first tile stores below
@@ -288,17 +300,17 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   }
   __syncthreads();
   {  // K (group 0) and V (group 1) of the block
-    TileCopy<kKeysPerWg> c;
-    const __bf16* src = (grp == 0 ? p.k : p.v) + (ur.k0 + k0) * kv_stride + (long)hkv * kD;
+    TileCopy<kKeysPerWg, D> c;
+    const __bf16* src = (grp == 0 ? p.k : p.v) + (ur.k0 + k0) * kv_stride + (long)hkv * D;
     c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
     c.store(kv_t + grp * kKeysPerWg * kRowElems, gtid);
   }
 
   const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
   const int key = wk0 + (lane & 31);
-  f32x16 dk_acc[4], dv_acc[4];
+  f32x16 dk_acc[TD], dv_acc[TD];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
+  for (int t = 0; t < TD; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
 
   const int s0 = CAUSAL ? (k0 / kQStep) : 0;
   const int nsteps_h = (nq + kQStep - 1) / kQStep - s0;
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   const int n_mine = (nsteps - grp + 1) / 2;   // this group's steps: grp, grp+2, ...
   const int n_per = (nsteps + 1) / 2 + 1;      // periods, the same for both groups
 
-  TileCopy<kQStep> qc, dc;
+  TileCopy<kQStep, D> qc, dc;
   float stat = 0.f;
   // first query row and head of this group's i-th step.  Steps run from the
   // last query rows back to the first, the G heads of a row block innermost:
@@ -318,7 +330,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   };
   auto fetch = [&](int i) {
     const int2 r = step_rows(i);
-    const long rowbase = (ur.q0 + r.x) * q_stride + (long)r.y * kD;
+    const long rowbase = (ur.q0 + r.x) * q_stride + (long)r.y * D;
     const int valid = min(nq - r.x, kQStep);
     qc.load(p.q + rowbase, q_stride, valid, gtid);
     dc.load(p.dout + rowbase, q_stride, valid, gtid);
@@ -342,13 +354,13 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
 
   f32x16 s_acc = {}, dp_acc = {};
   u32x4 p_pk[2] = {}, ds_pk[2] = {};
-  // MFMA phase slices, in groups of four for i = 0..7: S (k-slice i), dV,
-  // dP (k-slice i), dK, the last two for 16 queries qs = i / 4 and 32
-  // dimensions t = i % 4.  S and dP read two row operands each, dV and dK one
-  // transposed operand, so the LDS demand stays even over the phase.  Each
-  // slice's operands are read kAhead slices before its MFMA; scheduling
+  // MFMA phase slices, in groups of four for i = 0 .. D/16 - 1: S (k-slice
+  // i), dV, dP (k-slice i), dK, the last two for 16 queries qs = i / TD and
+  // 32 dimensions t = i % TD.  S and dP read two row operands each, dV and dK
+  // one transposed operand, so the LDS demand stays even over the phase.
+  // Each slice's operands are read kAhead slices before its MFMA; scheduling
   // barriers between the slices keep that order.
-  constexpr int kSlices = 32, kAhead = 3;
+  constexpr int kSlices = 4 * (D / 16), kAhead = 3;
   struct Opnd {
     bf16x8 a, b;
   };
@@ -362,10 +374,10 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     const int kr0 = (wave & 3) * 32;
     auto operand = [&](auto I) __attribute__((always_inline)) -> Opnd {
       constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
-      if constexpr (kind == 0) return {read_rows(qt, 0, n, lane), read_rows(k_t, kr0, n, lane)};
-      else if constexpr (kind == 2) return {read_rows(dt, 0, n, lane), read_rows(v_t, kr0, n, lane)};
-      else if constexpr (kind == 1) return {read_cols(dto, 16 * (n >> 2), 32 * (n & 3), lane), bf16x8{}};
-      else return {read_cols(qo, 16 * (n >> 2), 32 * (n & 3), lane), bf16x8{}};
+      if constexpr (kind == 0) return {L::read_rows(qt, 0, n, lane), L::read_rows(k_t, kr0, n, lane)};
+      else if constexpr (kind == 2) return {L::read_rows(dt, 0, n, lane), L::read_rows(v_t, kr0, n, lane)};
+      else if constexpr (kind == 1) return {L::read_cols(dto, 16 * (n / TD), 32 * (n % TD), lane), bf16x8{}};
+      else return {L::read_cols(qo, 16 * (n / TD), 32 * (n % TD), lane), bf16x8{}};
     };
     // ---- MFMA phase
     Opnd opnd[kAhead];
@@ -381,9 +393,9 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
       else if constexpr (kind == 2)
         dp_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : dp_acc);
       else if constexpr (kind == 1)
-        dv_acc[n & 3] = mfma32(o.a, __builtin_bit_cast(bf16x8, p_pk[n >> 2]), dv_acc[n & 3]);
+        dv_acc[n % TD] = mfma32(o.a, __builtin_bit_cast(bf16x8, p_pk[n / TD]), dv_acc[n % TD]);
       else
-        dk_acc[n & 3] = mfma32(o.a, __builtin_bit_cast(bf16x8, ds_pk[n >> 2]), dk_acc[n & 3]);
+        dk_acc[n % TD] = mfma32(o.a, __builtin_bit_cast(bf16x8, ds_pk[n / TD]), dk_acc[n % TD]);
       __builtin_amdgcn_sched_barrier(0);
     });
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -454,13 +466,13 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
 
   // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
   // [key][d] fp32 with rows padded by 16 bytes, so 16 lanes on 16 keys meet distinct banks
-  constexpr int kRedPitch = kD + 4;
+  constexpr int kRedPitch = D + 4;
   static_assert(sizeof(kv_t) >= kKeysPerWg * kRedPitch * sizeof(float), "reduction buffer");
   float* red = reinterpret_cast<float*>(kv_t);  // K and V are no longer needed
   const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
   auto xfer = [&](f32x16* acc, bool add) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TD; ++t)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g);
@@ -485,10 +497,10 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   if (grp == 0) xfer(dv_acc, true);
 
   if (grp == 0 && key < ur.k_write && key < k0 + kKeysPerWg) {
-    __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * kD;
-    __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * kD;
+    __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * D;
+    __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * D;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TD; ++t)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 a, c;
@@ -517,8 +529,12 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
 constexpr int kDqTile = 32;
 constexpr int kDqRows = 256;
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p) {
+  using L = Lds<D>;
+  constexpr int kRowElems = L::kRowElems;
+  constexpr int TD = D / 32;  // 32-wide d blocks of dQ^T
+  constexpr int KS = D / 16;  // 16-deep d slices of S^T and dP^T
   __shared__ __attribute__((aligned(1024))) __bf16 k_t[4][kDqTile * kRowElems];
   __shared__ __attribute__((aligned(1024))) __bf16 v_t[2][kDqTile * kRowElems];
 
@@ -542,16 +558,16 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   const UnitRows ur = unit_rows(p, b);
   const int nk = ur.nk, nq = ur.nq;
 
-  const long kv_stride = (long)p.Hkv * kD;
-  const long q_stride = (long)p.Hq * kD;
+  const long kv_stride = (long)p.Hkv * D;
+  const long q_stride = (long)p.Hq * D;
   const int q0 = qb * kDqRows;
   if (q0 >= nq) return;  // a packed sequence shorter than the longest; uniform
   const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);
   const int qrow = wrow0 + (lane & 31);
-  bf16x8 qf[kD / 16], df[kD / 16];
-  const long qoff = (ur.q0 + qrow) * q_stride + (long)h * kD;
+  bf16x8 qf[KS], df[KS];
+  const long qoff = (ur.q0 + qrow) * q_stride + (long)h * D;
 #pragma unroll
-  for (int ks = 0; ks < kD / 16; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     qf[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * g) : bf16x8{};
     df[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.dout + qoff + 16 * ks + 8 * g) : bf16x8{};
   }
@@ -563,7 +579,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   int kv_end = nk;
   if (CAUSAL) kv_end = min(nk, q0 + kDqRows);
   const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
-  const __bf16* src = (grp == 0 ? p.v : p.k) + ur.k0 * kv_stride + (long)hkv * kD;
+  const __bf16* src = (grp == 0 ? p.v : p.k) + ur.k0 * kv_stride + (long)hkv * D;
 
   // every buffer starts finite (the first dQ step multiplies zeros by K)
   for (int i = tid; i < 4 * kDqTile * kRowElems / 8; i += kBwPpThreads)
@@ -572,7 +588,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     reinterpret_cast<u32x4*>(&v_t[0][0])[i] = u32x4{};
   __syncthreads();
 
-  TileCopy<kDqTile> stage;
+  TileCopy<kDqTile, D> stage;
   auto fetch = [&](int j) {
     const int j0 = j * kDqTile;
     stage.load(src + (long)j0 * kv_stride, kv_stride, min(kv_end - j0, kDqTile), gtid);
@@ -585,17 +601,19 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  f32x16 acc[4];
+  f32x16 acc[TD];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+  for (int t = 0; t < TD; ++t) acc[t] = f32x16{};
   f32x16 s_acc = {}, dp_acc = {};
   u32x4 ds_pk[2] = {};
 
-  // MFMA phase slices: 0..15 are S and dP of tile j, alternating (one K or V
-  // row operand each), 16..23 dQ of tile j-1 (one K^T operand each).  Each
-  // slice's LDS operand is read kAhead slices before its MFMA; scheduling
-  // barriers between the slices keep that order.
-  constexpr int kSlices = 24, kAhead = 4, kMoveAt = 12;
+  // MFMA phase slices: 0 .. 2 KS - 1 are S and dP of tile j, alternating (one
+  // K or V row operand each), then 2 TD slices of dQ of tile j-1 (one K^T
+  // operand each).  Each slice's LDS operand is read kAhead slices before its
+  // MFMA; scheduling barriers between the slices keep that order.  The tile
+  // move sits after slice kMoveAt, half-way.
+  constexpr int kSD = 2 * KS;
+  constexpr int kSlices = kSD + 2 * TD, kAhead = 4, kMoveAt = kSlices / 2;
   auto period = [&](int j, auto J) {
     constexpr int j4 = decltype(J)::value;  // j % 4
     const __bf16* kt = kbuf(std::integral_constant<int, j4>{});
@@ -603,8 +621,8 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     const __bf16* kto = kbuf(std::integral_constant<int, j4 + 3>{});  // tile j-1
     auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
       constexpr int i = decltype(I)::value;
-      if constexpr (i < 16) return read_rows((i & 1) ? vt : kt, 0, i >> 1, lane);
-      else return read_cols(kto, 16 * ((i - 16) >> 2), 32 * ((i - 16) & 3), lane);
+      if constexpr (i < kSD) return L::read_rows((i & 1) ? vt : kt, 0, i >> 1, lane);
+      else return L::read_cols(kto, 16 * ((i - kSD) / TD), 32 * ((i - kSD) % TD), lane);
     };
     // ---- MFMA phase, with this group's tile move after slice kMoveAt
     bf16x8 opnd[kAhead];
@@ -615,14 +633,14 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
       constexpr int i = decltype(I)::value;
       const bf16x8 a = opnd[i % kAhead];
       if constexpr (i + kAhead < kSlices) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
-      if constexpr (i < 16) {
+      if constexpr (i < kSD) {
         constexpr int ks = i >> 1;
         if constexpr (i & 1)
           dp_acc = mfma32(a, df[ks], ks == 0 ? f32x16{} : dp_acc);
         else
           s_acc = mfma32(a, qf[ks], ks == 0 ? f32x16{} : s_acc);
       } else {
-        constexpr int hh = (i - 16) >> 2, t = (i - 16) & 3;
+        constexpr int hh = (i - kSD) / TD, t = (i - kSD) % TD;
         acc[t] = mfma32(a, __builtin_bit_cast(bf16x8, ds_pk[hh]), acc[t]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -692,7 +710,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   if (qrow < nq) {
     __bf16* row = p.dq + qoff;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TD; ++t)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 a;
@@ -716,43 +734,54 @@ int launched() {
 
 // Launches preprocess, dK/dV and dQ for the units p describes.  The LSE and
 // D workspace rows are [pre_b, Hq, pre_nq] (batched: B, Nq; packed: 1, Tq).
-int launch_backward(BwdParams p, const __bf16* o, const float* lse, int pre_b, long pre_nq,
-                    const int32_t* lse_rows, bool need_q, bool need_k, bool causal,
-                    hipStream_t st) {
+template <int D>
+int launch_backward_d(BwdParams p, const __bf16* o, const float* lse, int pre_b, long pre_nq,
+                      const int32_t* lse_rows, bool need_q, bool need_k, bool causal,
+                      hipStream_t st) {
+  constexpr long kPreRows = 256 / (D / 8);  // rows per preprocess block
   const long units8 = ((long)p.B * p.Hkv + kXcds - 1) / kXcds * kXcds;
   const int nblk_k = (p.Nk + kKeysPerWg - 1) / kKeysPerWg;
   const int nblk_q = (p.Nq + kDqRows - 1) / kDqRows;
   const long grid_k = units8 * nblk_k, grid_q = units8 * nblk_q * p.G;
   const long rows = (long)pre_b * pre_nq * p.Hq;
-  if (grid_k > INT_MAX || grid_q > INT_MAX || (rows + 15) / 16 > INT_MAX) return ATTN_ERR_TOO_LARGE;
+  const long grid_pre = (rows + kPreRows - 1) / kPreRows;
+  if (grid_k > INT_MAX || grid_q > INT_MAX || grid_pre > INT_MAX) return ATTN_ERR_TOO_LARGE;
   float* lse2 = const_cast<float*>(p.lse2);
   float* delta = const_cast<float*>(p.delta);
   if (need_q) {
-    hipLaunchKernelGGL(bwd_preprocess, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, o,
-                       p.dout, lse, lse2, delta, pre_b, p.Hq, (int)pre_nq, lse_rows);
+    hipLaunchKernelGGL(bwd_preprocess<D>, dim3((unsigned)grid_pre), dim3(256), 0, st, o, p.dout,
+                       lse, lse2, delta, pre_b, p.Hq, (int)pre_nq, lse_rows);
     if (int rc = launched()) return rc;
   }
   if (need_k) {
     p.nblk = nblk_k;
     if (causal)
-      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<true>, dim3((unsigned)grid_k), dim3(kBwPpThreads), 0,
-                         st, p);
+      hipLaunchKernelGGL((bwd_dkdv_pp_kernel<D, true>), dim3((unsigned)grid_k), dim3(kBwPpThreads),
+                         0, st, p);
     else
-      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<false>, dim3((unsigned)grid_k), dim3(kBwPpThreads), 0,
-                         st, p);
+      hipLaunchKernelGGL((bwd_dkdv_pp_kernel<D, false>), dim3((unsigned)grid_k), dim3(kBwPpThreads),
+                         0, st, p);
     if (int rc = launched()) return rc;
   }
   if (need_q) {
     p.nblk = nblk_q;
     if (causal)
-      hipLaunchKernelGGL(bwd_dq_pp_kernel<true>, dim3((unsigned)grid_q), dim3(kBwPpThreads), 0, st,
-                         p);
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, true>), dim3((unsigned)grid_q), dim3(kBwPpThreads),
+                         0, st, p);
     else
-      hipLaunchKernelGGL(bwd_dq_pp_kernel<false>, dim3((unsigned)grid_q), dim3(kBwPpThreads), 0,
-                         st, p);
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, false>), dim3((unsigned)grid_q), dim3(kBwPpThreads),
+                         0, st, p);
     if (int rc = launched()) return rc;
   }
   return ATTN_OK;
+}
+
+int launch_backward(int d, const BwdParams& p, const __bf16* o, const float* lse, int pre_b,
+                    long pre_nq, const int32_t* lse_rows, bool need_q, bool need_k, bool causal,
+                    hipStream_t st) {
+  if (d == 64)
+    return launch_backward_d<64>(p, o, lse, pre_b, pre_nq, lse_rows, need_q, need_k, causal, st);
+  return launch_backward_d<128>(p, o, lse, pre_b, pre_nq, lse_rows, need_q, need_k, causal, st);
 }
 
 }  // namespace
@@ -768,7 +797,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         float scale, int causal, const int32_t* seqlens_k, void* stream) {
   if (B < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SIZE;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
-  if (d != kD) return ATTN_ERR_HEAD_DIM;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SIZE;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
   const bool need_q = Nq > 0, need_k = Nk > 0;
@@ -781,8 +810,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
       (need_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))))
     return ATTN_ERR_ALIGN;
   const long rows = (long)B * Nq * Hq;
-  if (rows > INT_MAX || (long)B * Nk * Hkv > INT_MAX || (long)Nq * Hq * kD > INT_MAX / 2 ||
-      (long)Nk * Hkv * kD > INT_MAX / 2)
+  if (rows > INT_MAX || (long)B * Nk * Hkv > INT_MAX || (long)Nq * Hq * d > INT_MAX / 2 ||
+      (long)Nk * Hkv * d > INT_MAX / 2)
     return ATTN_ERR_TOO_LARGE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -807,7 +836,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.Nk = Nk;
   p.scale = scale;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  return launch_backward(p, static_cast<const __bf16*>(o), lse, B, Nq, nullptr, need_q, need_k,
+  return launch_backward(d, p, static_cast<const __bf16*>(o), lse, B, Nq, nullptr, need_q, need_k,
                          causal != 0, st);
 }
 
@@ -820,7 +849,7 @@ extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, cons
                                int causal, const int32_t* seq_order, void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_SIZE;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
-  if (d != kD) return ATTN_ERR_HEAD_DIM;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SIZE;
   if (num_seqs == 0 || (max_seqlen_q == 0 && max_seqlen_k == 0)) return ATTN_OK;
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
@@ -860,6 +889,6 @@ extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, cons
   p.Tq = total_q;
   p.scale = scale;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  return launch_backward(p, static_cast<const __bf16*>(o), lse, 1, total_q,
+  return launch_backward(d, p, static_cast<const __bf16*>(o), lse, 1, total_q,
                          cu_seqlens_q + num_seqs, need_q, need_k, causal != 0, st);
 }

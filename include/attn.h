@@ -32,7 +32,7 @@
  *   packed (varlen) form:
  *     q, o : bf16 [Tq, Hq, d]           k, v : bf16 [Tk, Hkv, d]
  *     lse  : fp32 [Hq, Tq],             Tq = cu_seqlens_q[num_seqs]
- * d must be 64 or 128 (128 for the backward).  q, k, v and o must be
+ * d must be 64 or 128 (forward and backward).  q, k, v and o must be
  * 16-byte aligned; lse 4-byte.
  * O is rounded to bf16 (round-to-nearest-even); LSE stays fp32.
  *
@@ -195,10 +195,10 @@ int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, i
  *               16-byte aligned, owned by the caller; its contents on entry do
  *               not matter and on return are unspecified.  Calls that overlap
  *               on the GPU need separate workspaces.
- *   d         : 128 (the only head dimension of the backward kernels).
+ *   d         : 64 or 128.
  * Results are deterministic: every dQ row is summed inside one workgroup and
  * every dK / dV row likewise, with no atomic adds.  Asynchronous on stream;
- * allocates nothing.  Returns an attn_status (ATTN_ERR_HEAD_DIM for d != 128;
+ * allocates nothing.  Returns an attn_status (ATTN_ERR_HEAD_DIM for d not 64 or 128;
  * ATTN_ERR_NULL / ATTN_ERR_ALIGN as for attn_fwd, including the workspace).
  * B == 0, or Nq == 0 and Nk == 0, is a no-op.
  */
@@ -226,7 +226,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *               sequence are not touched.
  *   workspace : attn_bwd_workspace_size(1, Hq, total_q) bytes, as for
  *               attn_bwd.
- *   d         : 128.
+ *   d         : 64 or 128.
  * Deterministic, asynchronous on stream, allocates nothing.  Returns an
  * attn_status as attn_bwd does (ATTN_ERR_NULL also for NULL cu_seqlens).
  * num_seqs == 0, or both max_seqlen bounds 0, is a no-op.

@@ -72,11 +72,19 @@ GRAD_REL_FRO = 1e-2
 GRAD_MAX_REL = 2e-2
 
 
-def grad_errors(got, ref):
+def grad_errors(got, ref, floor=0.0):
+    """Relative Frobenius and max errors of a gradient.
+
+    floor bounds the reference scale from below: a gradient that vanishes in
+    exact arithmetic (a softmax over one key is constant, so dQ and dK are 0)
+    is the difference of two roundings of terms of that size, and is measured
+    against them instead of against its own near-zero reference.
+    """
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    scale = max(np.abs(ref).max(), 1e-30)
-    return {"rel_fro": float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)),
+    scale = max(np.abs(ref).max(), floor, 1e-30)
+    norm = max(np.linalg.norm(ref), floor * np.sqrt(ref.size), 1e-30)
+    return {"rel_fro": float(np.linalg.norm(got - ref) / norm),
             "max_rel": float(np.abs(got - ref).max() / scale)}
 
 

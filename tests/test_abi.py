@@ -175,8 +175,9 @@ def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv
     (dict(dk=None), attn.ATTN_ERR_NULL),
     (dict(dv=None), attn.ATTN_ERR_NULL),
     (dict(ws=None), attn.ATTN_ERR_NULL),
-    (dict(d=64), attn.ATTN_ERR_HEAD_DIM),
     (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=192), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=256), attn.ATTN_ERR_HEAD_DIM),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_HEADS),
     (dict(Hkv=0), attn.ATTN_ERR_HEADS),
     (dict(B=-1), attn.ATTN_ERR_SIZE),
@@ -215,7 +216,8 @@ def _bwd_varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=F
     (dict(q=None), attn.ATTN_ERR_NULL),
     (dict(ws=None), attn.ATTN_ERR_NULL),
     (dict(dk=None), attn.ATTN_ERR_NULL),
-    (dict(d=64), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=32), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=192), attn.ATTN_ERR_HEAD_DIM),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_HEADS),
     (dict(S=-1), attn.ATTN_ERR_SIZE),
     (dict(Tq=-1), attn.ATTN_ERR_SIZE),

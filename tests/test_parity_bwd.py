@@ -3,7 +3,8 @@
 The backward consumes the GPU forward's own O and LSE (as in training), and a
 seeded upstream gradient dO.  Small shapes are compared on every element of
 dQ, dK and dV; they span several key and query tiles, ragged tails,
-Nq != Nk, GQA groups and key padding.  At the benchmark's size one whole
+Nq != Nk, GQA groups and key padding, at head dimensions 128 and 64.  At the
+headline benchmark's size and at the d = 64 batch workload's, one whole
 (batch, KV head) slice -- its query heads' dQ and the KV head's dK, dV -- is
 compared element by element.  The packed (varlen) entry point is checked on
 small ragged batches in full (with a zero-length sequence, lq != lk, GQA and
@@ -47,10 +48,10 @@ def _fwd_bwd(q, k, v, do, scale, causal, seqlens):
     return dq, dk, dv
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal,padded", SMALL)
-def test_backward_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded):
-    d = 128
-    seed = 9000 + B * 31 + Nq * 7 + Nk + Hq * 3 + int(causal)
+def test_backward_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded, d):
+    seed = 9000 + B * 31 + Nq * 7 + Nk + Hq * 3 + int(causal) + d
     q, k, v = inputs.make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=2.0)
     do = inputs.make_dout(q.shape, seed + 1)
     seqlens = None
@@ -60,22 +61,33 @@ def test_backward_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded):
         if B > 1:
             seqlens[1] = Nk
     scale = 1.0 / math.sqrt(d)
-    print(f"[parity-bwd] B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} causal={causal} padded={padded}",
-          flush=True)
+    print(f"[parity-bwd] B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} "
+          f"padded={padded}", flush=True)
     dq, dk, dv = _fwd_bwd(q, k, v, do, scale, causal, seqlens)
     rq, rk, rv = oracle.attention_backward(to_np64(q), to_np64(k), to_np64(v), to_np64(do), scale,
                                            causal, None if seqlens is None else seqlens.numpy(),
                                            workers=8)
+    floors = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    if Nk == 1:
+        # One key: P = 1 in every row, so dS = dP - D vanishes in exact
+        # arithmetic and dQ, dK are rounding residues of dP and D = <dO, O>;
+        # they are measured against the size of those cancelled terms.
+        o1 = np.repeat(to_np64(v), Hq // Hkv, axis=2)  # with one key, O = V exactly
+        o1 = np.broadcast_to(o1, do.shape)
+        dmax = float(np.abs(oracle.softmax_backward_delta(o1, to_np64(do))).max())
+        floors["dq"] = scale * dmax * float(np.abs(to_np64(k)).max())
+        floors["dk"] = scale * dmax * float(np.abs(to_np64(q)).max())
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        assert_grad_parity(grad_errors(to_np64(got), ref), name)
+        assert_grad_parity(grad_errors(to_np64(got), ref, floors[name]), name)
     if padded:  # keys past a batch element's length get exactly zero gradient
         sl = seqlens.numpy()
         for b in range(B):
             assert (dk[b, sl[b]:] == 0).all() and (dv[b, sl[b]:] == 0).all()
 
 
-def test_backward_is_deterministic():
-    q, k, v = inputs.make_qkv(2, 700, 700, 8, 2, 128, 9100, q_mult=3.0)
+@pytest.mark.parametrize("d", [128, 64])
+def test_backward_is_deterministic(d):
+    q, k, v = inputs.make_qkv(2, 700, 700, 8, 2, d, 9100, q_mult=3.0)
     do = inputs.make_dout(q.shape, 9101)
     a = _fwd_bwd(q, k, v, do, 0.088, True, None)
     b = _fwd_bwd(q, k, v, do, 0.088, True, None)
@@ -83,16 +95,17 @@ def test_backward_is_deterministic():
         assert torch.equal(x, y)
 
 
-def test_backward_full_size_slice():
-    """The benchmark's workload; one (batch, KV head) slice compared in full."""
-    w = inputs.WORKLOADS[inputs.HEADLINE]
+@pytest.mark.parametrize("wname", [inputs.HEADLINE, "batch64_h16_n1024_d64"])
+def test_backward_full_size_slice(wname):
+    """A benchmark workload at full size; one (batch, KV head) slice compared in full."""
+    w = inputs.WORKLOADS[wname]
     x = inputs.workload_inputs(w)
     do = inputs.make_dout(x["q"].shape, w.seed + 77)
     print(f"[parity-bwd] full size {w.name}", flush=True)
     dq, dk, dv = _fwd_bwd(x["q"], x["k"], x["v"], do, w.scale, w.causal, None)
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
     G = w.Hq // w.Hkv
-    b, hkv = 1, 3
+    b, hkv = min(1, w.B - 1), min(3, w.Hkv - 1)
     hs = slice(hkv * G, (hkv + 1) * G)
     q = to_np64(x["q"][b:b + 1, :, hs])
     k = to_np64(x["k"][b:b + 1, :, hkv:hkv + 1])
@@ -125,19 +138,19 @@ VARLEN = [
 ]
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("lq,lk,Hq,Hkv,causal", VARLEN)
-def test_backward_varlen_small_full_oracle(lq, lk, Hq, Hkv, causal):
-    d = 128
+def test_backward_varlen_small_full_oracle(lq, lk, Hq, Hkv, causal, d):
     lq = torch.tensor(lq, dtype=torch.int32)
     lk = lq.clone() if lk is None else torch.tensor(lk, dtype=torch.int32)
     cq, ck = inputs.cu_from_lengths(lq), inputs.cu_from_lengths(lk)
     Tq, Tk = int(cq[-1]), int(ck[-1])
-    seed = 9300 + Tq + 3 * Tk + Hq + int(causal)
+    seed = 9300 + Tq + 3 * Tk + Hq + int(causal) + d
     q, _, _ = inputs.make_packed_qkv(Tq, 1, Hq, Hkv, d, seed, q_mult=2.0)
     _, k, v = inputs.make_packed_qkv(1, Tk, Hq, Hkv, d, seed + 1)
     do = inputs.make_dout(q.shape, seed + 2)
     scale = 1.0 / math.sqrt(d)
-    print(f"[parity-bwd] varlen lq={lq.tolist()} lk={lk.tolist()} Hq={Hq} Hkv={Hkv} "
+    print(f"[parity-bwd] varlen lq={lq.tolist()} lk={lk.tolist()} Hq={Hq} Hkv={Hkv} d={d} "
           f"causal={causal}", flush=True)
     dq, dk, dv = _fwd_bwd_varlen(q, k, v, do, cq, ck, int(lq.max()), int(lk.max()), scale, causal)
     rq, rk, rv = oracle.attention_backward_varlen(to_np64(q), to_np64(k), to_np64(v), to_np64(do),
