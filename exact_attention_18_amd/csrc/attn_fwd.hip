@@ -119,6 +119,8 @@ struct Params {
   int Hq, Hkv, G;
   int Nq, Nk;  // packed form: max_seqlen_q, max_seqlen_k
   int nqb;     // query blocks per (sequence, head)
+  int items;   // work items (the ids decode_work reads)
+  int paired;  // 1: a ping-pong workgroup runs two items of one unit (the i-th longest and shortest)
   int pack;    // query heads of one KV group per workgroup (1, 2, 4 or 8; 1 unless d = 128)
   int num_seqs;
   float c;  // scale * log2(e)
@@ -137,19 +139,21 @@ constexpr int kMaxSparseTiles = 4096;  // key tiles a block-sparse launch may vi
 // workgroups resident on one XCD stream the same K/V through its L2, and every
 // XCD gets a like share of every batch element, also when their lengths
 // differ (longest-processing-time-first order of FlashAttention-4
-// (papercache summary), section 3.3).  The grid holds ceil(units / 8) * 8
-// units; ids past the last unit are padding.
+// (papercache summary), section 3.3).  An id is a work item; a workgroup of
+// XCD x takes only ids x + 8 r (one id, its own, when the grid has one
+// workgroup per item).  The ids cover ceil(units / 8) * 8 units; ids past the
+// last unit are padding.
 struct WorkItem {
   int b, hkv, qb, gi;
   bool valid;
 };
 
-__device__ __forceinline__ WorkItem decode_work(const Params& p, bool causal) {
+__device__ __forceinline__ WorkItem decode_work(const Params& p, bool causal, int id) {
   const int units = p.num_seqs * p.Hkv;
   const int groups = p.G / p.pack;  // workgroups per query block of a unit
   const int per_unit = p.nqb * groups;
-  const int x = blockIdx.x % kXcds;
-  const int r = blockIdx.x / kXcds;
+  const int x = id % kXcds;
+  const int r = id / kXcds;
   const int u = (r / per_unit) * kXcds + x;
   const int item = r % per_unit;
   const int qbi = item / groups;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   const int g = lane >> 5;
 
   // ---- work item (see decode_work)
-  const WorkItem wi = decode_work(p, CAUSAL);
+  const WorkItem wi = decode_work(p, CAUSAL, blockIdx.x);
   if (!wi.valid) return;  // grid padding; uniform over the workgroup
   const int b = (VARLEN && p.seq_order != nullptr)
                     ? min(max(p.seq_order[wi.b], 0), p.num_seqs - 1)
@@ -558,373 +562,395 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // ---- work item (see decode_work)
-  const WorkItem wi = decode_work(p, CAUSAL);
-  if (!wi.valid) return;  // grid padding; uniform over the workgroup
-  const int b = (VARLEN && p.seq_order != nullptr)
-                    ? min(max(p.seq_order[wi.b], 0), p.num_seqs - 1)
-                    : wi.b;
-  const int hkv = wi.hkv, qb = wi.qb, gi = wi.gi;
-  // The workgroup takes P query heads of the KV group, 256 / P rows of each:
-  // chunk c holds rows (c % cph) * 32 .. +31 of head gi + c / cph.  The two
-  // waves of a SIMD (chunks 2s, 2s+1) always share their causal extent.
-  const int P = SPARSE ? 1 : p.pack;
-  const int cph = kPpWaves / P;               // 32-row chunks per head
-  const int rows_h = kRowsPerWave * cph;      // query rows per head
-  const int h = hkv * p.G + gi + chunk / cph;
-
-  int q_len, nk;
-  long q_row0, k_row0, lse_base, lse_hstride;
-  if (VARLEN) {
-    const int qs = p.cu_q[b], qe = p.cu_q[b + 1];
-    const int ks = p.cu_k[b], ke = p.cu_k[b + 1];
-    q_len = min(max(qe - qs, 0), p.Nq);
-    nk = min(max(ke - ks, 0), p.Nk);
-    q_row0 = qs;
-    k_row0 = ks;
-    lse_base = qs;
-    lse_hstride = p.cu_q[p.num_seqs];
-  } else {
-    q_len = p.Nq;
-    nk = p.Nk;
-    if (p.seqlens_k != nullptr) nk = min(max(p.seqlens_k[b], 0), p.Nk);
-    q_row0 = (long)b * p.Nq;
-    k_row0 = (long)b * p.Nk;
-    lse_base = (long)b * p.Hq * p.Nq;
-    lse_hstride = p.Nq;
-  }
-  const int q0 = qb * rows_h;
-  if (q0 >= q_len) return;  // uniform over the workgroup, before any barrier
-
-  const long q_stride = (long)p.Hq * DQK;
-  const long o_stride = (long)p.Hq * DV;
-  const long k_stride = (long)p.Hkv * DQK;
-  const long v_stride = (long)p.Hkv * DV;
-  const __bf16* qbase = p.q + q_row0 * q_stride + (long)h * DQK;
-  const __bf16* kbase = p.k + k_row0 * k_stride + (long)hkv * DQK;
-  const __bf16* vbase = p.v + k_row0 * v_stride + (long)hkv * DV;
-
-  const int wrow0 = q0 + (chunk % cph) * kRowsPerWave;
-  const int qrow = wrow0 + l32;
-  bf16x8 qf[T::KS];
-#pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks)
-    qf[ks] = qrow < q_len
-                 ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
-                 : bf16x8{};
-
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // qf ready before any tile load is in flight
-  int kv_end = nk;
-  if (CAUSAL) kv_end = min(nk, min(q0 + rows_h, q_len));
-  const int n_tiles = (kv_end + T::BC - 1) / T::BC;
-
-  // Block-sparse: the key tiles whose 128-key block is set in either of this
-  // workgroup's two 128-row mask rows, compacted in order into an LDS list
-  // (FlashAttention notes (xwysyy), "Block-Sparse FlashAttention": zero
-  // blocks are skipped).  Dense launches visit tiles 0 .. n_tiles-1.
-  __shared__ int tile_list[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int tile_list[SPARSE ? kMaxSparseTiles : 1];  // block-sparse work list
   __shared__ int wave_count[SPARSE ? kPpWaves : 1];
-  int n_iter = n_tiles;
-  const uint8_t* mrow = nullptr;  // this wave's mask row
-  if constexpr (SPARSE) {
-    const int hm = p.mask_heads == 1 ? 0 : h;
-    const uint8_t* mask0 = p.block_mask + ((long)hm * p.nbq + q0 / kSparseBlock) * p.nbk;
-    const bool two_rows = q0 / kSparseBlock + 1 < p.nbq;
-    // (waves whose rows lie past Nq read the last mask row; their rows are not stored)
-    mrow = p.block_mask + ((long)hm * p.nbq + min(wrow0 / kSparseBlock, p.nbq - 1)) * p.nbk;
-    n_iter = 0;
-    for (int c0 = 0; c0 < n_tiles; c0 += kPpThreads) {
-      const int j = c0 + tid;
-      const int mc = j * T::BC / kSparseBlock;
-      const bool vis = j < n_tiles && (mask0[mc] != 0 || (two_rows && mask0[p.nbk + mc] != 0));
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
-      if (lane == 0) wave_count[wave] = __builtin_popcountll(bal);
-      __syncthreads();
-      int before = n_iter;
-      for (int w = 0; w < wave; ++w) before += wave_count[w];
-      const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-      if (vis) tile_list[before + rank] = j;
-      for (int w = 0; w < kPpWaves; ++w) n_iter += wave_count[w];
-      __syncthreads();
+
+  // One work item: a query block of P query heads of one (sequence, KV head)
+  // unit.  Returns at the same point in every wave.
+  auto run_item = [&](const int item) __attribute__((always_inline)) {
+    // ---- work item (see decode_work)
+    const WorkItem wi = decode_work(p, CAUSAL, item);
+    if (!wi.valid) return;  // grid padding; uniform over the workgroup
+    const int b = (VARLEN && p.seq_order != nullptr)
+                      ? min(max(p.seq_order[wi.b], 0), p.num_seqs - 1)
+                      : wi.b;
+    const int hkv = wi.hkv, qb = wi.qb, gi = wi.gi;
+    // The workgroup takes P query heads of the KV group, 256 / P rows of each:
+    // chunk c holds rows (c % cph) * 32 .. +31 of head gi + c / cph.  The two
+    // waves of a SIMD (chunks 2s, 2s+1) always share their causal extent.
+    const int P = SPARSE ? 1 : p.pack;
+    const int cph = kPpWaves / P;               // 32-row chunks per head
+    const int rows_h = kRowsPerWave * cph;      // query rows per head
+    const int h = hkv * p.G + gi + chunk / cph;
+
+    int q_len, nk;
+    long q_row0, k_row0, lse_base, lse_hstride;
+    if (VARLEN) {
+      const int qs = p.cu_q[b], qe = p.cu_q[b + 1];
+      const int ks = p.cu_k[b], ke = p.cu_k[b + 1];
+      q_len = min(max(qe - qs, 0), p.Nq);
+      nk = min(max(ke - ks, 0), p.Nk);
+      q_row0 = qs;
+      k_row0 = ks;
+      lse_base = qs;
+      lse_hstride = p.cu_q[p.num_seqs];
+    } else {
+      q_len = p.Nq;
+      nk = p.Nk;
+      if (p.seqlens_k != nullptr) nk = min(max(p.seqlens_k[b], 0), p.Nk);
+      q_row0 = (long)b * p.Nq;
+      k_row0 = (long)b * p.Nk;
+      lse_base = (long)b * p.Hq * p.Nq;
+      lse_hstride = p.Nq;
     }
-  }
-  // Key tile visited at list position t.
-  auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE) return tile_list[t]; else return t;
-  };
+    const int q0 = qb * rows_h;
+    if (q0 >= q_len) return;  // uniform over the workgroup, before any barrier
 
-  auto k_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
-    const int rem16 = c % (16 * (DQK / 8));
-    *row = 16 * (c / (16 * (DQK / 8))) + rem16 % 16;
-    *colb = (rem16 / 16) * 16;
-  };
-  auto v_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
-    const int w = c % (DV / 2);
-    *row = 4 * (c / (DV / 2)) + (w % 8) / 2;
-    *colb = (16 * (w / 8) + 8 * (w % 2)) * 2;
-  };
-  // Group 0 moves V tiles, group 1 K tiles; wave w of a group fills the
-  // 1 KB slot runs (i*4 + w%4)*64 .. +63 of the tile (16 bytes per lane).
-  // Rows past kv_end read as zero (buffer range check) and are masked.
-  const int gw = wave & 3;
-  const bool fetch_v = grp == 0;
-  const int nch = fetch_v ? CHV : CHK;  // chunks per lane of this group's tiles
-  const uint32_t row_bytes = static_cast<uint32_t>(fetch_v ? v_stride : k_stride) * 2u;
-  uint32_t goff[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = (i * 4 + gw) * 64 + lane;
-    int row, colb;
-    if (fetch_v) v_slot(c, &row, &colb); else k_slot(c, &row, &colb);
-    goff[i] = row * row_bytes + colb;
-  }
-  const __bf16* gbase = fetch_v ? vbase : kbase;
-  u32x4 stage[CH];
-  // loads key tile `tile` (an index into the key sequence, not into the work list)
-  auto load_tile_at = [&](int tile) __attribute__((always_inline)) {
-    const int kv0 = tile * T::BC;
-    const int nrows = min(kv_end - kv0, T::BC);
-    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(gbase + (long)kv0 * (row_bytes / 2)), (short)0, nrows * (int)row_bytes,
-        kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-      if (i < nch)
-        stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, goff[i], 0, 0));
-  };
-  auto store_chunk = [&](__bf16* dst, auto C) __attribute__((always_inline)) {
-    constexpr int i = decltype(C)::value;
-    *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
-  };
-  auto store_tile = [&](__bf16* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-      if (i < nch) *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
-  };
+    const long q_stride = (long)p.Hq * DQK;
+    const long o_stride = (long)p.Hq * DV;
+    const long k_stride = (long)p.Hkv * DQK;
+    const long v_stride = (long)p.Hkv * DV;
+    const __bf16* qbase = p.q + q_row0 * q_stride + (long)h * DQK;
+    const __bf16* kbase = p.k + k_row0 * k_stride + (long)hkv * DQK;
+    const __bf16* vbase = p.v + k_row0 * v_stride + (long)hkv * DV;
 
-  const int k_lane = ((l32 >> 4) * (DQK / 8) + g) * 128 + (l32 & 15) * 8;
-  const int v_lane = g * TV::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
+    const int wrow0 = q0 + (chunk % cph) * kRowsPerWave;
+    const int qrow = wrow0 + l32;
+    bf16x8 qf[T::KS];
+  #pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+      qf[ks] = qrow < q_len
+                   ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
+                   : bf16x8{};
 
-  const float c = p.c;
-  // Tiles crossing the key tail or the diagonal (or lying wholly above this
-  // wave's rows, which the mask then empties) are masked.
-  // This wave's rows see the tile's 128-key block (block-sparse; else always).
-  auto block_visible = [&](int tile) __attribute__((always_inline)) -> bool {
-    if constexpr (SPARSE) return mrow[tile * T::BC / kSparseBlock] != 0; else return true;
-  };
-  auto needs_mask = [&](int tile) __attribute__((always_inline)) {
-    const int kv0 = tile * T::BC;
-    return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0) || !block_visible(tile);
-  };
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // qf ready before any tile load is in flight
+    int kv_end = nk;
+    if (CAUSAL) kv_end = min(nk, min(q0 + rows_h, q_len));
+    const int n_tiles = (kv_end + T::BC - 1) / T::BC;
 
-  f32x16 sv[T::KT];
-  u32x4 pv_op[T::KT][2];
-  f32x16 acc[TV::DT];
-#pragma unroll
-  for (int dt = 0; dt < TV::DT; ++dt) acc[dt] = f32x16{};
-#pragma unroll
-  for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  float m_use = 0.f;
-
-  // ---- MFMA phase: S_j = K_j Q^T (key blocks interleaved), then O += P_{j-1} V_{j-1}.
-  constexpr int kS = T::KT * T::KS;
-  constexpr int kPv = T::KT * 2 * TV::DT;
-  constexpr int kAhead = 3;       // LDS operand reads run this many MFMAs ahead
-  constexpr int kMoveFirst = 4;   // tile-store slots inside the MFMA phase
-  // 8 slices apart where that fits, else spread evenly over the phase
-  constexpr int kMoveStride =
-      kMoveFirst + (CH - 1) * 8 < kS + kPv ? 8 : (kS + kPv - kMoveFirst) / CH;
-  static_assert(kMoveFirst + (CH - 1) * kMoveStride < kS + kPv, "move slots");
-  // mid(c) runs after slice kMoveFirst + c*kMoveStride (tile chunk c moves to LDS there).
-  auto mphase = [&](const __bf16* kb, const __bf16* vb, auto&& mid) __attribute__((always_inline)) {
-    constexpr int n0 = kS;          // slices [0, kS): scores; [kS, kS + kPv): P V
-    constexpr int nsl = kS + kPv;
-    auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
-      constexpr int i = decltype(I)::value;
-      if constexpr (i < n0) {
-        constexpr int kt = i % T::KT, ks = i / T::KT;
-        return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (DQK / 8) + 2 * ks) * 128);
-      } else {
-        constexpr int s = i - n0;
-        constexpr int kt = s / (2 * TV::DT), hh = (s / TV::DT) % 2, dt = s % TV::DT;
-        const __bf16* p0 = vb + v_lane + (8 * kt + 4 * hh) * TV::QUAD + dt * 128;
-        return read_tr_pair(p0, p0 + 2 * TV::QUAD);
+    // Block-sparse: the key tiles whose 128-key block is set in either of this
+    // workgroup's two 128-row mask rows, compacted in order into an LDS list
+    // (FlashAttention notes (xwysyy), "Block-Sparse FlashAttention": zero
+    // blocks are skipped).  Dense launches visit tiles 0 .. n_tiles-1.
+    int n_iter = n_tiles;
+    const uint8_t* mrow = nullptr;  // this wave's mask row
+    if constexpr (SPARSE) {
+      const int hm = p.mask_heads == 1 ? 0 : h;
+      const uint8_t* mask0 = p.block_mask + ((long)hm * p.nbq + q0 / kSparseBlock) * p.nbk;
+      const bool two_rows = q0 / kSparseBlock + 1 < p.nbq;
+      // (waves whose rows lie past Nq read the last mask row; their rows are not stored)
+      mrow = p.block_mask + ((long)hm * p.nbq + min(wrow0 / kSparseBlock, p.nbq - 1)) * p.nbk;
+      n_iter = 0;
+      for (int c0 = 0; c0 < n_tiles; c0 += kPpThreads) {
+        const int j = c0 + tid;
+        const int mc = j * T::BC / kSparseBlock;
+        const bool vis = j < n_tiles && (mask0[mc] != 0 || (two_rows && mask0[p.nbk + mc] != 0));
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
+        if (lane == 0) wave_count[wave] = __builtin_popcountll(bal);
+        __syncthreads();
+        int before = n_iter;
+        for (int w = 0; w < wave; ++w) before += wave_count[w];
+        const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (vis) tile_list[before + rank] = j;
+        for (int w = 0; w < kPpWaves; ++w) n_iter += wave_count[w];
+        __syncthreads();
       }
+    }
+    // Key tile visited at list position t.
+    auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
+      if constexpr (SPARSE) return tile_list[t]; else return t;
     };
-    bf16x8 opnd[kAhead];
-    static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
-      if constexpr (decltype(I)::value < nsl) opnd[decltype(I)::value] = operand(I);
-    });
-    static_for<0, nsl>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = decltype(I)::value;
-      const bf16x8 a = opnd[i % kAhead];
-      if constexpr (i + kAhead < nsl) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
-      if constexpr (i < n0) {
-        constexpr int kt = i % T::KT, ks = i / T::KT;
-        sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
-      } else {
-        constexpr int s = i - n0;
-        constexpr int kt = s / (2 * TV::DT), hh = (s / TV::DT) % 2, dt = s % TV::DT;
-        acc[dt] = mfma32(a, __builtin_bit_cast(bf16x8, pv_op[kt][hh]), acc[dt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i >= kMoveFirst && (i - kMoveFirst) % kMoveStride == 0 &&
-                    (i - kMoveFirst) / kMoveStride < CH) {
-        mid(std::integral_constant<int, (i - kMoveFirst) / kMoveStride>{});
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    });
-  };
-  auto apply_mask = [&](int tile) __attribute__((always_inline)) {
-    const int kv0 = tile * T::BC;
-    const bool bvis = block_visible(tile);
-#pragma unroll
-    for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool vis = bvis && key < nk && (!CAUSAL || key <= qrow);
-        if (!vis) sv[kt][r] = -INFINITY;
-      }
-  };
-  // ---- VALU phase: online softmax of S_j -> P_j, O rescale when the max moved.
-  auto vphase = [&](int j) __attribute__((always_inline)) {
-    const int tile = tile_of(j);
-    if (needs_mask(tile)) apply_mask(tile);
-    float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 32; e += 4) {
-      m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
-      m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
-    }
-    const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
-    // The rescale (new max, alpha, l and O scaled) runs only when some row's
-    // max grew by more than tau; the test is wave-uniform, and otherwise
-    // alpha would be exactly 1.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
-    }
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], c, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
-        ls0 += e0;
-        ls1 += e1;
-        const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-        uint32_t u = __builtin_bit_cast(uint32_t, pk);
-        asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
-        pv_op[kt][r >> 3][(r & 7) >> 1] = u;
-      }
-    asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
-    l_run += ls0 + ls1;
-  };
 
-  // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
-  // V_j at h = 2j+1, group 1 runs M_j at h = 2j+1 and V_j at h = 2j+2.  K_t
-  // lives in k[t%2], V_t in v[t%2].  Tiles move global -> VGPRs -> LDS:
-  // during M_j, between two MFMAs, group 0 stores V_j (loaded one period
-  // earlier) and group 1 stores K_{j+1}; at the start of V_j (block-sparse:
-  // at the end of M_j) they load V_{j+1} and K_{j+2}.  Each store is complete before the barrier that
-  // ends its phase, which precedes the first read of the tile.
-  constexpr bool kLoadInMfmaPhase = SPARSE;
-  auto kbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
-    if constexpr (decltype(I)::value % 2 == 0) return k_lds0; else return k_lds1;
-  };
-  auto vbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
-    if constexpr (decltype(I)::value % 2 == 0) return v_lds0; else return v_lds1;
-  };
-  auto barrier = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // One period: M_j (+ tile store and load), barrier, V_j, barrier.  At j = 0
-  // the P V adds zero (P and the V buffer it reads are zeroed first); at
-  // j = n_iter the scores come from a stale K tile and are never used.
-  auto period = [&](int j, auto J) __attribute__((always_inline)) {
-    constexpr int j2 = decltype(J)::value;  // j % 2
-    const int st = fetch_v ? j : j + 1;  // tile stored in this phase
-    // the tile loaded at the start of the VALU phase; looked up now, so that a
-    // work-list read (block-sparse) is done by then
-    const int next_tile = st + 1 < n_iter ? tile_of(st + 1) : 0;
-    __bf16* dst = fetch_v ? vbuf(std::integral_constant<int, j2>{}) : kbuf(std::integral_constant<int, j2 + 1>{});
-    // The staged tile goes to LDS one 16-byte chunk per lane at a time,
-    // spread over the MFMA phase; the next tile is loaded into the freed
-    // registers at the start of the VALU phase, which is the shorter one
-    // (dense), or right after the last chunk (block-sparse, whose VALU phase
-    // masks more tiles: there the MFMA-phase placement measured faster).
-    // Past the last tile the store is left unguarded: it writes stale
-    // registers into a buffer no later MFMA phase reads.
-    auto move = [&](auto C) __attribute__((always_inline)) {
-      constexpr int c = decltype(C)::value;
-      if (c < nch) store_chunk(dst, C);
-      if constexpr (kLoadInMfmaPhase && c == CH - 1) {
+    auto k_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
+      const int rem16 = c % (16 * (DQK / 8));
+      *row = 16 * (c / (16 * (DQK / 8))) + rem16 % 16;
+      *colb = (rem16 / 16) * 16;
+    };
+    auto v_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
+      const int w = c % (DV / 2);
+      *row = 4 * (c / (DV / 2)) + (w % 8) / 2;
+      *colb = (16 * (w / 8) + 8 * (w % 2)) * 2;
+    };
+    // Group 0 moves V tiles, group 1 K tiles; wave w of a group fills the
+    // 1 KB slot runs (i*4 + w%4)*64 .. +63 of the tile (16 bytes per lane).
+    // Rows past kv_end read as zero (buffer range check) and are masked.
+    const int gw = wave & 3;
+    const bool fetch_v = grp == 0;
+    const int nch = fetch_v ? CHV : CHK;  // chunks per lane of this group's tiles
+    const uint32_t row_bytes = static_cast<uint32_t>(fetch_v ? v_stride : k_stride) * 2u;
+    uint32_t goff[CH];
+  #pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = (i * 4 + gw) * 64 + lane;
+      int row, colb;
+      if (fetch_v) v_slot(c, &row, &colb); else k_slot(c, &row, &colb);
+      goff[i] = row * row_bytes + colb;
+    }
+    const __bf16* gbase = fetch_v ? vbase : kbase;
+    u32x4 stage[CH];
+    // loads key tile `tile` (an index into the key sequence, not into the work list)
+    auto load_tile_at = [&](int tile) __attribute__((always_inline)) {
+      const int kv0 = tile * T::BC;
+      const int nrows = min(kv_end - kv0, T::BC);
+      const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<__bf16*>(gbase + (long)kv0 * (row_bytes / 2)), (short)0, nrows * (int)row_bytes,
+          kBufferFlags);
+  #pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if (i < nch)
+          stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, goff[i], 0, 0));
+    };
+    auto store_chunk = [&](__bf16* dst, auto C) __attribute__((always_inline)) {
+      constexpr int i = decltype(C)::value;
+      *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
+    };
+    auto store_tile = [&](__bf16* dst) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if (i < nch) *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
+    };
+
+    const int k_lane = ((l32 >> 4) * (DQK / 8) + g) * 128 + (l32 & 15) * 8;
+    const int v_lane = g * TV::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
+
+    const float c = p.c;
+    // Tiles crossing the key tail or the diagonal (or lying wholly above this
+    // wave's rows, which the mask then empties) are masked.
+    // This wave's rows see the tile's 128-key block (block-sparse; else always).
+    auto block_visible = [&](int tile) __attribute__((always_inline)) -> bool {
+      if constexpr (SPARSE) return mrow[tile * T::BC / kSparseBlock] != 0; else return true;
+    };
+    auto needs_mask = [&](int tile) __attribute__((always_inline)) {
+      const int kv0 = tile * T::BC;
+      return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0) || !block_visible(tile);
+    };
+
+    f32x16 sv[T::KT];
+    u32x4 pv_op[T::KT][2];
+    f32x16 acc[TV::DT];
+  #pragma unroll
+    for (int dt = 0; dt < TV::DT; ++dt) acc[dt] = f32x16{};
+  #pragma unroll
+    for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    float m_use = 0.f;
+
+    // ---- MFMA phase: S_j = K_j Q^T (key blocks interleaved), then O += P_{j-1} V_{j-1}.
+    constexpr int kS = T::KT * T::KS;
+    constexpr int kPv = T::KT * 2 * TV::DT;
+    constexpr int kAhead = 3;       // LDS operand reads run this many MFMAs ahead
+    constexpr int kMoveFirst = 4;   // tile-store slots inside the MFMA phase
+    // 8 slices apart where that fits, else spread evenly over the phase
+    constexpr int kMoveStride =
+        kMoveFirst + (CH - 1) * 8 < kS + kPv ? 8 : (kS + kPv - kMoveFirst) / CH;
+    static_assert(kMoveFirst + (CH - 1) * kMoveStride < kS + kPv, "move slots");
+    // mid(c) runs after slice kMoveFirst + c*kMoveStride (tile chunk c moves to LDS there).
+    auto mphase = [&](const __bf16* kb, const __bf16* vb, auto&& mid) __attribute__((always_inline)) {
+      constexpr int n0 = kS;          // slices [0, kS): scores; [kS, kS + kPv): P V
+      constexpr int nsl = kS + kPv;
+      auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < n0) {
+          constexpr int kt = i % T::KT, ks = i / T::KT;
+          return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (DQK / 8) + 2 * ks) * 128);
+        } else {
+          constexpr int s = i - n0;
+          constexpr int kt = s / (2 * TV::DT), hh = (s / TV::DT) % 2, dt = s % TV::DT;
+          const __bf16* p0 = vb + v_lane + (8 * kt + 4 * hh) * TV::QUAD + dt * 128;
+          return read_tr_pair(p0, p0 + 2 * TV::QUAD);
+        }
+      };
+      bf16x8 opnd[kAhead];
+      static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
+        if constexpr (decltype(I)::value < nsl) opnd[decltype(I)::value] = operand(I);
+      });
+      static_for<0, nsl>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        const bf16x8 a = opnd[i % kAhead];
+        if constexpr (i + kAhead < nsl) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
+        if constexpr (i < n0) {
+          constexpr int kt = i % T::KT, ks = i / T::KT;
+          sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
+        } else {
+          constexpr int s = i - n0;
+          constexpr int kt = s / (2 * TV::DT), hh = (s / TV::DT) % 2, dt = s % TV::DT;
+          acc[dt] = mfma32(a, __builtin_bit_cast(bf16x8, pv_op[kt][hh]), acc[dt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i >= kMoveFirst && (i - kMoveFirst) % kMoveStride == 0 &&
+                      (i - kMoveFirst) / kMoveStride < CH) {
+          mid(std::integral_constant<int, (i - kMoveFirst) / kMoveStride>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    };
+    auto apply_mask = [&](int tile) __attribute__((always_inline)) {
+      const int kv0 = tile * T::BC;
+      const bool bvis = block_visible(tile);
+  #pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = bvis && key < nk && (!CAUSAL || key <= qrow);
+          if (!vis) sv[kt][r] = -INFINITY;
+        }
+    };
+    // ---- VALU phase: online softmax of S_j -> P_j, O rescale when the max moved.
+    auto vphase = [&](int j) __attribute__((always_inline)) {
+      const int tile = tile_of(j);
+      if (needs_mask(tile)) apply_mask(tile);
+      float m0 = -INFINITY, m1 = -INFINITY;
+  #pragma unroll
+      for (int e = 0; e < 32; e += 4) {
+        m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
+        m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
+      }
+      const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
+      // The rescale (new max, alpha, l and O scaled) runs only when some row's
+      // max grew by more than tau; the test is wave-uniform, and otherwise
+      // alpha would be exactly 1.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        l_run *= alpha;
+  #pragma unroll
+        for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
+      }
+      float ls0 = 0.f, ls1 = 0.f;
+  #pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt)
+  #pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], c, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
+          ls0 += e0;
+          ls1 += e1;
+          const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+          uint32_t u = __builtin_bit_cast(uint32_t, pk);
+          asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
+          pv_op[kt][r >> 3][(r & 7) >> 1] = u;
+        }
+      asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
+      l_run += ls0 + ls1;
+    };
+
+    // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
+    // V_j at h = 2j+1, group 1 runs M_j at h = 2j+1 and V_j at h = 2j+2.  K_t
+    // lives in k[t%2], V_t in v[t%2].  Tiles move global -> VGPRs -> LDS:
+    // during M_j, between two MFMAs, group 0 stores V_j (loaded one period
+    // earlier) and group 1 stores K_{j+1}; at the start of V_j (block-sparse:
+    // at the end of M_j) they load V_{j+1} and K_{j+2}.  Each store is complete before the barrier that
+    // ends its phase, which precedes the first read of the tile.
+    constexpr bool kLoadInMfmaPhase = SPARSE;
+    auto kbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
+      if constexpr (decltype(I)::value % 2 == 0) return k_lds0; else return k_lds1;
+    };
+    auto vbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
+      if constexpr (decltype(I)::value % 2 == 0) return v_lds0; else return v_lds1;
+    };
+    auto barrier = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // One period: M_j (+ tile store and load), barrier, V_j, barrier.  At j = 0
+    // the P V adds zero (P and the V buffer it reads are zeroed first); at
+    // j = n_iter the scores come from a stale K tile and are never used.
+    auto period = [&](int j, auto J) __attribute__((always_inline)) {
+      constexpr int j2 = decltype(J)::value;  // j % 2
+      const int st = fetch_v ? j : j + 1;  // tile stored in this phase
+      // the tile loaded at the start of the VALU phase; looked up now, so that a
+      // work-list read (block-sparse) is done by then
+      const int next_tile = st + 1 < n_iter ? tile_of(st + 1) : 0;
+      __bf16* dst = fetch_v ? vbuf(std::integral_constant<int, j2>{}) : kbuf(std::integral_constant<int, j2 + 1>{});
+      // The staged tile goes to LDS one 16-byte chunk per lane at a time,
+      // spread over the MFMA phase; the next tile is loaded into the freed
+      // registers at the start of the VALU phase, which is the shorter one
+      // (dense), or right after the last chunk (block-sparse, whose VALU phase
+      // masks more tiles: there the MFMA-phase placement measured faster).
+      // Past the last tile the store is left unguarded: it writes stale
+      // registers into a buffer no later MFMA phase reads.
+      auto move = [&](auto C) __attribute__((always_inline)) {
+        constexpr int c = decltype(C)::value;
+        if (c < nch) store_chunk(dst, C);
+        if constexpr (kLoadInMfmaPhase && c == CH - 1) {
+          if (st + 1 < n_iter) load_tile_at(next_tile);
+        }
+      };
+      // The wave in its MFMA phase gets issue priority over the other wave of
+      // its SIMD, so a ready MFMA is not held behind that wave's softmax.
+      __builtin_amdgcn_s_setprio(3);
+      mphase(kbuf(std::integral_constant<int, j2>{}), vbuf(std::integral_constant<int, j2 + 1>{}), move);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this phase's LDS stores are done
+      barrier();
+      if constexpr (!kLoadInMfmaPhase) {
         if (st + 1 < n_iter) load_tile_at(next_tile);
       }
+      if (j < n_iter) vphase(j);
+      barrier();
     };
-    // The wave in its MFMA phase gets issue priority over the other wave of
-    // its SIMD, so a ready MFMA is not held behind that wave's softmax.
-    __builtin_amdgcn_s_setprio(3);
-    mphase(kbuf(std::integral_constant<int, j2>{}), vbuf(std::integral_constant<int, j2 + 1>{}), move);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this phase's LDS stores are done
-    barrier();
-    if constexpr (!kLoadInMfmaPhase) {
-      if (st + 1 < n_iter) load_tile_at(next_tile);
+
+  #pragma unroll
+    for (int kt = 0; kt < T::KT; ++kt) pv_op[kt][0] = pv_op[kt][1] = u32x4{};
+    for (int i = tid; i < TV::V_ELEMS / 8; i += kPpThreads)
+      reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
+    // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
+    if (fetch_v) {
+      if (n_iter > 0) load_tile_at(tile_of(0));
+    } else {
+      if (n_iter > 0) { load_tile_at(tile_of(0)); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
+      if (n_iter > 1) load_tile_at(tile_of(1));
     }
-    if (j < n_iter) vphase(j);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
+    if (grp == 1) barrier();  // group 1 starts half a period late
+    int j = 0;
+    for (; j + 1 <= n_iter; j += 2) {
+      period(j, std::integral_constant<int, 0>{});
+      period(j + 1, std::integral_constant<int, 1>{});
+    }
+    if (j <= n_iter) period(j, std::integral_constant<int, 0>{});
+    if (grp == 0) barrier();
+
+    const float l_tot = pair_sum(l_run);
+    if (qrow < q_len) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* orow = p.o + (q_row0 + qrow) * o_stride + (long)h * DV;
+  #pragma unroll
+      for (int dt = 0; dt < TV::DT; ++dt)
+  #pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 ov;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * rq + 4 * g) = ov;
+        }
+      if (g == 0)
+        p.lse[lse_base + (long)h * lse_hstride + qrow] =
+            l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   };
 
-#pragma unroll
-  for (int kt = 0; kt < T::KT; ++kt) pv_op[kt][0] = pv_op[kt][1] = u32x4{};
-  for (int i = tid; i < TV::V_ELEMS / 8; i += kPpThreads)
-    reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
-  // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
-  if (fetch_v) {
-    if (n_iter > 0) load_tile_at(tile_of(0));
+  // Paired items: workgroup w of XCD x (w = x + 8 m) runs, within that XCD's
+  // items x + 8 r (decode_work), the i-th and the (n-1-i)-th item of one unit
+  // of n items, so a pair costs about the same under the causal mask (items
+  // run longest first) and the hardware still balances pairs between CUs.
+  // One launch gap and one pipeline fill less per pair.  Otherwise each
+  // workgroup runs the item of its own id.
+  if (p.paired) {
+    const int n = p.nqb * (p.G / p.pack);  // items per unit
+    const int xcd = blockIdx.x % kXcds, m = blockIdx.x / kXcds;
+    const int u = m / (n / 2), i = m % (n / 2);
+    run_item((u * n + i) * kXcds + xcd);
+    __syncthreads();  // the first item's LDS reads are done before the second's stores
+    run_item((u * n + n - 1 - i) * kXcds + xcd);
   } else {
-    if (n_iter > 0) { load_tile_at(tile_of(0)); __builtin_amdgcn_s_waitcnt(kWaitVm0); store_tile(k_lds0); }
-    if (n_iter > 1) load_tile_at(tile_of(1));
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  barrier();
-  if (grp == 1) barrier();  // group 1 starts half a period late
-  int j = 0;
-  for (; j + 1 <= n_iter; j += 2) {
-    period(j, std::integral_constant<int, 0>{});
-    period(j + 1, std::integral_constant<int, 1>{});
-  }
-  if (j <= n_iter) period(j, std::integral_constant<int, 0>{});
-  if (grp == 0) barrier();
-
-  const float l_tot = pair_sum(l_run);
-  if (qrow < q_len) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = p.o + (q_row0 + qrow) * o_stride + (long)h * DV;
-#pragma unroll
-    for (int dt = 0; dt < TV::DT; ++dt)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * rq + 4 * g) = ov;
-      }
-    if (g == 0)
-      p.lse[lse_base + (long)h * lse_hstride + qrow] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    run_item(blockIdx.x);
   }
 }
 
@@ -986,12 +1012,27 @@ constexpr bool use_pp(int d) { return d == 128; }
 // serves 256 rows.
 constexpr int pp_pack(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
 
+// Ping-pong launches pair the items of a unit when a unit has an even count,
+// except block-sparse ones, whose item costs follow the mask rather than the
+// diagonal (pairing measured 2 % slower there).  Returns the workgroups to
+// launch and sets p.items and p.paired.
+int pp_grid(Params& p, long items, bool pair) {
+  p.items = static_cast<int>(items);
+  const int n = p.nqb * (p.G / p.pack);
+  p.paired = (pair && n % 2 == 0) ? 1 : 0;
+  return static_cast<int>(p.paired ? items / 2 : items);
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
-int launch_one(const Params& p, int grid, hipStream_t stream) {
+int launch_one(Params p, int grid, hipStream_t stream) {
   (void)hipGetLastError();  // clear a stale error so the check below is ours
-  if constexpr (use_pp(D))
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, D, CAUSAL, VARLEN>), dim3(grid), dim3(kPpThreads), 0,
+  p.items = grid;
+  p.paired = 0;
+  if constexpr (use_pp(D)) {
+    const int wgs = pp_grid(p, grid, true);
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, D, CAUSAL, VARLEN>), dim3(wgs), dim3(kPpThreads), 0,
                        stream, p);
+  }
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream,
                        p);
@@ -1106,14 +1147,15 @@ extern "C" int attn_fwd_dims(const void* q, const void* k, const void* v, void* 
   p.pack = pack;
   p.num_seqs = B;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const unsigned wgs = static_cast<unsigned>(pp_grid(p, grid, true));
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, true, false>), dim3((unsigned)grid),
-                       dim3(kPpThreads), 0, st, p);
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, true, false>), dim3(wgs), dim3(kPpThreads), 0,
+                       st, p);
   else
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, false, false>), dim3((unsigned)grid),
-                       dim3(kPpThreads), 0, st, p);
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<192, 128, false, false>), dim3(wgs), dim3(kPpThreads), 0,
+                       st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     attn_detail::last_hip_error = static_cast<int>(e);
@@ -1159,13 +1201,14 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
   p.mask_heads = mask_heads;
   p.nbq = (Nq + kSparseBlock - 1) / kSparseBlock;
   p.nbk = (Nk + kSparseBlock - 1) / kSparseBlock;
+  const unsigned wgs = static_cast<unsigned>(pp_grid(p, grid, false));
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, true, false, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, true, false, true>), dim3(wgs),
                        dim3(kPpThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, false, false, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, false, false, true>), dim3(wgs),
                        dim3(kPpThreads), 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
