@@ -76,6 +76,7 @@ struct BwdParams {
   int B, Hq, Hkv, G, Nq, Nk;  // packed form: B = sequences, Nq/Nk = the longest lengths
   long Tq;                    // packed form: total query rows (the LSE row stride per head)
   int nblk;             // key blocks (dK/dV) or query blocks (dQ) per (batch, head)
+  int paired;           // 1: a workgroup runs the i-th and (n-1-i)-th item of a unit of n
   float c;              // scale * log2(e)
   float scale;
 };
@@ -123,6 +124,26 @@ __device__ __forceinline__ UnitRows unit_rows(const BwdParams& p, int b) {
   r.nk = __builtin_amdgcn_readfirstlane(r.nk);
   r.k_write = __builtin_amdgcn_readfirstlane(r.k_write);
   return r;
+}
+
+// Work items of a launch: item id w belongs to XCD w % 8 (the hardware sends
+// workgroup id w there), and XCD x takes the items of its units in order,
+// longest first under the causal mask.  When p.paired is set, workgroup w
+// runs two items of one unit of n: the i-th and the (n-1-i)-th, which cost
+// about the same under the causal mask, with one launch and one pipeline
+// fill less than two workgroups; the hardware still deals the pairs
+// dynamically.  Otherwise workgroup w runs item w.
+template <class F>
+__device__ __forceinline__ void run_items(const BwdParams& p, int n, F&& run_item) {
+  if (p.paired) {
+    const int xcd = blockIdx.x % kXcds, m = blockIdx.x / kXcds;
+    const int u = m / (n / 2), i = m % (n / 2);
+    run_item((u * n + i) * kXcds + xcd);
+    __syncthreads();  // the first item's LDS reads are done before the second's stores
+    run_item((u * n + n - 1 - i) * kXcds + xcd);
+  } else {
+    run_item(static_cast<int>(blockIdx.x));
+  }
 }
 
 // LDS tile layout.  Rows (D bf16, D/8 16-byte units) come in groups of 16; a
@@ -279,241 +300,243 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   const __bf16* k_t = kv_t;
   const __bf16* v_t = kv_t + kKeysPerWg * kRowElems;
 
-  const int units = p.B * p.Hkv;
-  const int x = blockIdx.x % kXcds, rr = blockIdx.x / kXcds;
-  const int u = (rr / p.nblk) * kXcds + x;
-  if (u >= units) return;  // grid padding; uniform over the workgroup
-  const int kb = rr % p.nblk;
-  const int b = u / p.Hkv, hkv = u % p.Hkv;
-  const UnitRows ur = unit_rows(p, b);
-  const int nk = ur.nk, nq = ur.nq;
-  const int k0 = kb * kKeysPerWg;
-  if (k0 >= ur.k_write) return;  // a packed sequence shorter than the longest; uniform
-  const long kv_stride = (long)p.Hkv * D;
-  const long q_stride = (long)p.Hq * D;
+  run_items(p, p.nblk, [&](const int id) __attribute__((always_inline)) {
+    const int units = p.B * p.Hkv;
+    const int x = id % kXcds, rr = id / kXcds;
+    const int u = (rr / p.nblk) * kXcds + x;
+    if (u >= units) return;  // grid padding; uniform over the workgroup
+    const int kb = rr % p.nblk;
+    const int b = u / p.Hkv, hkv = u % p.Hkv;
+    const UnitRows ur = unit_rows(p, b);
+    const int nk = ur.nk, nq = ur.nq;
+    const int k0 = kb * kKeysPerWg;
+    if (k0 >= ur.k_write) return;  // a packed sequence shorter than the longest; uniform
+    const long kv_stride = (long)p.Hkv * D;
+    const long q_stride = (long)p.Hq * D;
 
-  // every tile buffer starts finite (periods without a step multiply zeros by
-  // it); the barrier orders these stores before the first tile stores below
-  for (int i = tid; i < 2 * 2 * kQStep * kRowElems / 8; i += kBwPpThreads) {
-    reinterpret_cast<u32x4*>(&q_t[0][0][0])[i] = u32x4{};
-    reinterpret_cast<u32x4*>(&do_t[0][0][0])[i] = u32x4{};
-  }
-  __syncthreads();
-  {  // K (group 0) and V (group 1) of the block
-    TileCopy<kKeysPerWg, D> c;
-    const __bf16* src = (grp == 0 ? p.k : p.v) + (ur.k0 + k0) * kv_stride + (long)hkv * D;
-    c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
-    c.store(kv_t + grp * kKeysPerWg * kRowElems, gtid);
-  }
-
-  const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
-  const int key = wk0 + (lane & 31);
-  f32x16 dk_acc[TD], dv_acc[TD];
-#pragma unroll
-  for (int t = 0; t < TD; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
-
-  const int s0 = CAUSAL ? (k0 / kQStep) : 0;
-  const int nsteps_h = (nq + kQStep - 1) / kQStep - s0;
-  const int nsteps = nk > k0 ? max(nsteps_h, 0) * p.G : 0;
-  const int n_mine = (nsteps - grp + 1) / 2;   // this group's steps: grp, grp+2, ...
-  const int n_per = (nsteps + 1) / 2 + 1;      // periods, the same for both groups
-
-  TileCopy<kQStep, D> qc, dc;
-  float stat = 0.f;
-  // first query row and head of this group's i-th step.  Steps run from the
-  // last query rows back to the first, the G heads of a row block innermost:
-  // the workgroups of one (batch, KV head), which run side by side on one XCD,
-  // then read the same Q and dO rows at about the same time, from L2.
-  auto step_rows = [&](int i) {
-    const int s = 2 * i + grp;
-    return make_int2((s0 + nsteps_h - 1 - s / p.G) * kQStep, hkv * p.G + s % p.G);
-  };
-  auto fetch = [&](int i) {
-    const int2 r = step_rows(i);
-    const long rowbase = (ur.q0 + r.x) * q_stride + (long)r.y * D;
-    const int valid = min(nq - r.x, kQStep);
-    qc.load(p.q + rowbase, q_stride, valid, gtid);
-    dc.load(p.dout + rowbase, q_stride, valid, gtid);
-    if (gtid < 2 * kQStep) {
-      const int row = r.x + (gtid & 31);
-      const long sidx = ur.lse0 + ur.lse_h * r.y + row;
-      stat = (row < nq) ? (gtid < kQStep ? p.lse2[sidx] : p.delta[sidx])
-                          : (gtid < kQStep ? INFINITY : 0.f);
+    // every tile buffer starts finite (periods without a step multiply zeros by
+    // it); the barrier orders these stores before the first tile stores below
+    for (int i = tid; i < 2 * 2 * kQStep * kRowElems / 8; i += kBwPpThreads) {
+      reinterpret_cast<u32x4*>(&q_t[0][0][0])[i] = u32x4{};
+      reinterpret_cast<u32x4*>(&do_t[0][0][0])[i] = u32x4{};
     }
-  };
-  auto put = [&](int buf) {
-    qc.store(q_t[grp][buf], gtid);
-    dc.store(do_t[grp][buf], gtid);
-    if (gtid < 2 * kQStep) st_t[grp][buf][gtid] = stat;
-  };
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    __syncthreads();
+    {  // K (group 0) and V (group 1) of the block
+      TileCopy<kKeysPerWg, D> c;
+      const __bf16* src = (grp == 0 ? p.k : p.v) + (ur.k0 + k0) * kv_stride + (long)hkv * D;
+      c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
+      c.store(kv_t + grp * kKeysPerWg * kRowElems, gtid);
+    }
 
-  f32x16 s_acc = {}, dp_acc = {};
-  u32x4 p_pk[2] = {}, ds_pk[2] = {};
-  // MFMA phase slices, in groups of four for i = 0 .. D/16 - 1: S (k-slice
-  // i), dV, dP (k-slice i), dK, the last two for 16 queries qs = i / TD and
-  // 32 dimensions t = i % TD.  S and dP read two row operands each, dV and dK
-  // one transposed operand, so the LDS demand stays even over the phase.
-  // Each slice's operands are read kAhead slices before its MFMA; scheduling
-  // barriers between the slices keep that order.
-  constexpr int kSlices = 4 * (D / 16), kAhead = 3;
-  struct Opnd {
-    bf16x8 a, b;
-  };
-  // One period: MFMA phase, barrier, VALU phase, barrier.
-  auto period = [&](int i, auto par) {
-    constexpr int B0 = decltype(par)::value;  // i % 2: buffer of step i
-    const __bf16* qt = q_t[grp][B0];
-    const __bf16* dt = do_t[grp][B0];
-    const __bf16* qo = q_t[grp][B0 ^ 1];  // step i-1
-    const __bf16* dto = do_t[grp][B0 ^ 1];
-    const int kr0 = (wave & 3) * 32;
-    auto operand = [&](auto I) __attribute__((always_inline)) -> Opnd {
-      constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
-      if constexpr (kind == 0) return {L::read_rows(qt, 0, n, lane), L::read_rows(k_t, kr0, n, lane)};
-      else if constexpr (kind == 2) return {L::read_rows(dt, 0, n, lane), L::read_rows(v_t, kr0, n, lane)};
-      else if constexpr (kind == 1) return {L::read_cols(dto, 16 * (n / TD), 32 * (n % TD), lane), bf16x8{}};
-      else return {L::read_cols(qo, 16 * (n / TD), 32 * (n % TD), lane), bf16x8{}};
+    const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
+    const int key = wk0 + (lane & 31);
+    f32x16 dk_acc[TD], dv_acc[TD];
+  #pragma unroll
+    for (int t = 0; t < TD; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
+
+    const int s0 = CAUSAL ? (k0 / kQStep) : 0;
+    const int nsteps_h = (nq + kQStep - 1) / kQStep - s0;
+    const int nsteps = nk > k0 ? max(nsteps_h, 0) * p.G : 0;
+    const int n_mine = (nsteps - grp + 1) / 2;   // this group's steps: grp, grp+2, ...
+    const int n_per = (nsteps + 1) / 2 + 1;      // periods, the same for both groups
+
+    TileCopy<kQStep, D> qc, dc;
+    float stat = 0.f;
+    // first query row and head of this group's i-th step.  Steps run from the
+    // last query rows back to the first, the G heads of a row block innermost:
+    // the workgroups of one (batch, KV head), which run side by side on one XCD,
+    // then read the same Q and dO rows at about the same time, from L2.
+    auto step_rows = [&](int i) {
+      const int s = 2 * i + grp;
+      return make_int2((s0 + nsteps_h - 1 - s / p.G) * kQStep, hkv * p.G + s % p.G);
     };
-    // ---- MFMA phase
-    Opnd opnd[kAhead];
-    static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
-      opnd[decltype(I)::value] = operand(I);
-    });
-    static_for<0, kSlices>([&](auto I) __attribute__((always_inline)) {
-      constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
-      const Opnd o = opnd[sl % kAhead];
-      if constexpr (sl + kAhead < kSlices) opnd[sl % kAhead] = operand(std::integral_constant<int, sl + kAhead>{});
-      if constexpr (kind == 0)
-        s_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : s_acc);
-      else if constexpr (kind == 2)
-        dp_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : dp_acc);
-      else if constexpr (kind == 1)
-        dv_acc[n % TD] = mfma32(o.a, __builtin_bit_cast(bf16x8, p_pk[n / TD]), dv_acc[n % TD]);
-      else
-        dk_acc[n % TD] = mfma32(o.a, __builtin_bit_cast(bf16x8, ds_pk[n / TD]), dk_acc[n % TD]);
+    auto fetch = [&](int i) {
+      const int2 r = step_rows(i);
+      const long rowbase = (ur.q0 + r.x) * q_stride + (long)r.y * D;
+      const int valid = min(nq - r.x, kQStep);
+      qc.load(p.q + rowbase, q_stride, valid, gtid);
+      dc.load(p.dout + rowbase, q_stride, valid, gtid);
+      if (gtid < 2 * kQStep) {
+        const int row = r.x + (gtid & 31);
+        const long sidx = ur.lse0 + ur.lse_h * r.y + row;
+        stat = (row < nq) ? (gtid < kQStep ? p.lse2[sidx] : p.delta[sidx])
+                            : (gtid < kQStep ? INFINITY : 0.f);
+      }
+    };
+    auto put = [&](int buf) {
+      qc.store(q_t[grp][buf], gtid);
+      dc.store(do_t[grp][buf], gtid);
+      if (gtid < 2 * kQStep) st_t[grp][buf][gtid] = stat;
+    };
+    auto barrier = [&]() {
       __builtin_amdgcn_sched_barrier(0);
-    });
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    barrier();
-    // ---- VALU phase: P, dS of step i (zero when this group has no step i);
-    // this group's step i+1 is loaded meanwhile and stored into the buffer
-    // step i-1 used (its last reader was the MFMA phase just finished).  A
-    // step whose rows all see all of this wave's keys skips the mask.
-    const bool more = i + 1 < n_mine;
-    if (more) fetch(i + 1);
-    if (i < n_mine) {
-      const int i0 = step_rows(i).x;
-      const float* l2t = st_t[grp][B0];
-      const float* ddt = st_t[grp][B0] + kQStep;
-      const bool full = wk0 + 32 <= nk && (!CAUSAL || wk0 + 31 <= i0);
-      auto block = [&](bool masked) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int qi = 8 * r4 + 4 * g;
-          const float4 l2 = *reinterpret_cast<const float4*>(l2t + qi);
-          const float4 dd = *reinterpret_cast<const float4*>(ddt + qi);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
-            const float dv_ = e == 0 ? dd.x : e == 1 ? dd.y : e == 2 ? dd.z : dd.w;
-            const bool vis = !masked || (key < nk && (!CAUSAL || key <= i0 + qi + e));
-            const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -lv)) : 0.f;
-            pv[e] = pe;
-            dsv[e] = pe * (dp_acc[r] - dv_);
-          }
-          const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
-          const bf16x2 d01 = {(__bf16)dsv[0], (__bf16)dsv[1]}, d23 = {(__bf16)dsv[2], (__bf16)dsv[3]};
-          p_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, p01);
-          p_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
-          ds_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, d01);
-          ds_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
-        }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    f32x16 s_acc = {}, dp_acc = {};
+    u32x4 p_pk[2] = {}, ds_pk[2] = {};
+    // MFMA phase slices, in groups of four for i = 0 .. D/16 - 1: S (k-slice
+    // i), dV, dP (k-slice i), dK, the last two for 16 queries qs = i / TD and
+    // 32 dimensions t = i % TD.  S and dP read two row operands each, dV and dK
+    // one transposed operand, so the LDS demand stays even over the phase.
+    // Each slice's operands are read kAhead slices before its MFMA; scheduling
+    // barriers between the slices keep that order.
+    constexpr int kSlices = 4 * (D / 16), kAhead = 3;
+    struct Opnd {
+      bf16x8 a, b;
+    };
+    // One period: MFMA phase, barrier, VALU phase, barrier.
+    auto period = [&](int i, auto par) {
+      constexpr int B0 = decltype(par)::value;  // i % 2: buffer of step i
+      const __bf16* qt = q_t[grp][B0];
+      const __bf16* dt = do_t[grp][B0];
+      const __bf16* qo = q_t[grp][B0 ^ 1];  // step i-1
+      const __bf16* dto = do_t[grp][B0 ^ 1];
+      const int kr0 = (wave & 3) * 32;
+      auto operand = [&](auto I) __attribute__((always_inline)) -> Opnd {
+        constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
+        if constexpr (kind == 0) return {L::read_rows(qt, 0, n, lane), L::read_rows(k_t, kr0, n, lane)};
+        else if constexpr (kind == 2) return {L::read_rows(dt, 0, n, lane), L::read_rows(v_t, kr0, n, lane)};
+        else if constexpr (kind == 1) return {L::read_cols(dto, 16 * (n / TD), 32 * (n % TD), lane), bf16x8{}};
+        else return {L::read_cols(qo, 16 * (n / TD), 32 * (n % TD), lane), bf16x8{}};
       };
-      if (full)
-        block(false);
-      else
-        block(true);
-    } else {
-      p_pk[0] = p_pk[1] = ds_pk[0] = ds_pk[1] = u32x4{};
+      // ---- MFMA phase
+      Opnd opnd[kAhead];
+      static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
+        opnd[decltype(I)::value] = operand(I);
+      });
+      static_for<0, kSlices>([&](auto I) __attribute__((always_inline)) {
+        constexpr int sl = decltype(I)::value, n = sl >> 2, kind = sl & 3;
+        const Opnd o = opnd[sl % kAhead];
+        if constexpr (sl + kAhead < kSlices) opnd[sl % kAhead] = operand(std::integral_constant<int, sl + kAhead>{});
+        if constexpr (kind == 0)
+          s_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : s_acc);
+        else if constexpr (kind == 2)
+          dp_acc = mfma32(o.a, o.b, n == 0 ? f32x16{} : dp_acc);
+        else if constexpr (kind == 1)
+          dv_acc[n % TD] = mfma32(o.a, __builtin_bit_cast(bf16x8, p_pk[n / TD]), dv_acc[n % TD]);
+        else
+          dk_acc[n % TD] = mfma32(o.a, __builtin_bit_cast(bf16x8, ds_pk[n / TD]), dk_acc[n % TD]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      // ---- VALU phase: P, dS of step i (zero when this group has no step i);
+      // this group's step i+1 is loaded meanwhile and stored into the buffer
+      // step i-1 used (its last reader was the MFMA phase just finished).  A
+      // step whose rows all see all of this wave's keys skips the mask.
+      const bool more = i + 1 < n_mine;
+      if (more) fetch(i + 1);
+      if (i < n_mine) {
+        const int i0 = step_rows(i).x;
+        const float* l2t = st_t[grp][B0];
+        const float* ddt = st_t[grp][B0] + kQStep;
+        const bool full = wk0 + 32 <= nk && (!CAUSAL || wk0 + 31 <= i0);
+        auto block = [&](bool masked) __attribute__((always_inline)) {
+  #pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int qi = 8 * r4 + 4 * g;
+            const float4 l2 = *reinterpret_cast<const float4*>(l2t + qi);
+            const float4 dd = *reinterpret_cast<const float4*>(ddt + qi);
+            float pv[4], dsv[4];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
+              const float dv_ = e == 0 ? dd.x : e == 1 ? dd.y : e == 2 ? dd.z : dd.w;
+              const bool vis = !masked || (key < nk && (!CAUSAL || key <= i0 + qi + e));
+              const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -lv)) : 0.f;
+              pv[e] = pe;
+              dsv[e] = pe * (dp_acc[r] - dv_);
+            }
+            const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
+            const bf16x2 d01 = {(__bf16)dsv[0], (__bf16)dsv[1]}, d23 = {(__bf16)dsv[2], (__bf16)dsv[3]};
+            p_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, p01);
+            p_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
+            ds_pk[r4 >> 1][2 * (r4 & 1)] = __builtin_bit_cast(uint32_t, d01);
+            ds_pk[r4 >> 1][2 * (r4 & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
+          }
+        };
+        if (full)
+          block(false);
+        else
+          block(true);
+      } else {
+        p_pk[0] = p_pk[1] = ds_pk[0] = ds_pk[1] = u32x4{};
+      }
+      if (more) put(B0 ^ 1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+    };
+
+    if (n_mine > 0) {
+      fetch(0);
+      put(0);
     }
-    if (more) put(B0 ^ 1);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    barrier();
-  };
+    __syncthreads();
+    if (grp == 1) barrier();  // group 1 runs half a period behind
+    int i = 0;
+    for (; i + 1 < n_per; i += 2) {
+      period(i, std::integral_constant<int, 0>{});
+      period(i + 1, std::integral_constant<int, 1>{});
+    }
+    if (i < n_per) period(i, std::integral_constant<int, 0>{});
+    if (grp == 0) barrier();
+    __syncthreads();
 
-  if (n_mine > 0) {
-    fetch(0);
-    put(0);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __syncthreads();
-  if (grp == 1) barrier();  // group 1 runs half a period behind
-  int i = 0;
-  for (; i + 1 < n_per; i += 2) {
-    period(i, std::integral_constant<int, 0>{});
-    period(i + 1, std::integral_constant<int, 1>{});
-  }
-  if (i < n_per) period(i, std::integral_constant<int, 0>{});
-  if (grp == 0) barrier();
-  __syncthreads();
-
-  // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
-  // [key][d] fp32 with rows padded by 16 bytes, so 16 lanes on 16 keys meet distinct banks
-  constexpr int kRedPitch = D + 4;
-  static_assert(sizeof(kv_t) >= kKeysPerWg * kRedPitch * sizeof(float), "reduction buffer");
-  float* red = reinterpret_cast<float*>(kv_t);  // K and V are no longer needed
-  const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
-  auto xfer = [&](f32x16* acc, bool add) {
-#pragma unroll
-    for (int t = 0; t < TD; ++t)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g);
-        if (add) {
-          const float4 o = *slot;
-          acc[t][4 * r4 + 0] += o.x;
-          acc[t][4 * r4 + 1] += o.y;
-          acc[t][4 * r4 + 2] += o.z;
-          acc[t][4 * r4 + 3] += o.w;
-        } else {
-          *slot = make_float4(acc[t][4 * r4 + 0], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2],
-                              acc[t][4 * r4 + 3]);
+    // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
+    // [key][d] fp32 with rows padded by 16 bytes, so 16 lanes on 16 keys meet distinct banks
+    constexpr int kRedPitch = D + 4;
+    static_assert(sizeof(kv_t) >= kKeysPerWg * kRedPitch * sizeof(float), "reduction buffer");
+    float* red = reinterpret_cast<float*>(kv_t);  // K and V are no longer needed
+    const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
+    auto xfer = [&](f32x16* acc, bool add) {
+  #pragma unroll
+      for (int t = 0; t < TD; ++t)
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g);
+          if (add) {
+            const float4 o = *slot;
+            acc[t][4 * r4 + 0] += o.x;
+            acc[t][4 * r4 + 1] += o.y;
+            acc[t][4 * r4 + 2] += o.z;
+            acc[t][4 * r4 + 3] += o.w;
+          } else {
+            *slot = make_float4(acc[t][4 * r4 + 0], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2],
+                                acc[t][4 * r4 + 3]);
+          }
         }
-      }
-  };
-  if (grp == 1) xfer(dk_acc, false);
-  __syncthreads();
-  if (grp == 0) xfer(dk_acc, true);
-  __syncthreads();
-  if (grp == 1) xfer(dv_acc, false);
-  __syncthreads();
-  if (grp == 0) xfer(dv_acc, true);
+    };
+    if (grp == 1) xfer(dk_acc, false);
+    __syncthreads();
+    if (grp == 0) xfer(dk_acc, true);
+    __syncthreads();
+    if (grp == 1) xfer(dv_acc, false);
+    __syncthreads();
+    if (grp == 0) xfer(dv_acc, true);
 
-  if (grp == 0 && key < ur.k_write && key < k0 + kKeysPerWg) {
-    __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * D;
-    __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * D;
-#pragma unroll
-    for (int t = 0; t < TD; ++t)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 a, c;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (__bf16)(dk_acc[t][4 * r4 + e] * p.scale);
-          c[e] = (__bf16)dv_acc[t][4 * r4 + e];
+    if (grp == 0 && key < ur.k_write && key < k0 + kKeysPerWg) {
+      __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * D;
+      __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * D;
+  #pragma unroll
+      for (int t = 0; t < TD; ++t)
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 a, c;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = (__bf16)(dk_acc[t][4 * r4 + e] * p.scale);
+            c[e] = (__bf16)dv_acc[t][4 * r4 + e];
+          }
+          const int dcol = 32 * t + 8 * r4 + 4 * g;
+          *reinterpret_cast<bf16x4*>(dkrow + dcol) = a;
+          *reinterpret_cast<bf16x4*>(dvrow + dcol) = c;
         }
-        const int dcol = 32 * t + 8 * r4 + 4 * g;
-        *reinterpret_cast<bf16x4*>(dkrow + dcol) = a;
-        *reinterpret_cast<bf16x4*>(dvrow + dcol) = c;
-      }
-  }
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -545,180 +568,182 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   const int gtid = tid & (kBwThreads - 1);
   const int g = lane >> 5;
 
-  const int units = p.B * p.Hkv;
-  const int per_unit = p.nblk * p.G;
-  const int x = blockIdx.x % kXcds, rr = blockIdx.x / kXcds;
-  const int u = (rr / per_unit) * kXcds + x;
-  if (u >= units) return;
-  const int item = rr % per_unit;
-  const int qbi = item / p.G, gi = item % p.G;
-  const int qb = CAUSAL ? (p.nblk - 1 - qbi) : qbi;
-  const int b = u / p.Hkv, hkv = u % p.Hkv;
-  const int h = hkv * p.G + gi;
-  const UnitRows ur = unit_rows(p, b);
-  const int nk = ur.nk, nq = ur.nq;
+  run_items(p, p.nblk * p.G, [&](const int id) __attribute__((always_inline)) {
+    const int units = p.B * p.Hkv;
+    const int per_unit = p.nblk * p.G;
+    const int x = id % kXcds, rr = id / kXcds;
+    const int u = (rr / per_unit) * kXcds + x;
+    if (u >= units) return;
+    const int item = rr % per_unit;
+    const int qbi = item / p.G, gi = item % p.G;
+    const int qb = CAUSAL ? (p.nblk - 1 - qbi) : qbi;
+    const int b = u / p.Hkv, hkv = u % p.Hkv;
+    const int h = hkv * p.G + gi;
+    const UnitRows ur = unit_rows(p, b);
+    const int nk = ur.nk, nq = ur.nq;
 
-  const long kv_stride = (long)p.Hkv * D;
-  const long q_stride = (long)p.Hq * D;
-  const int q0 = qb * kDqRows;
-  if (q0 >= nq) return;  // a packed sequence shorter than the longest; uniform
-  const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);
-  const int qrow = wrow0 + (lane & 31);
-  bf16x8 qf[KS], df[KS];
-  const long qoff = (ur.q0 + qrow) * q_stride + (long)h * D;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * g) : bf16x8{};
-    df[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.dout + qoff + 16 * ks + 8 * g) : bf16x8{};
-  }
-  const long sidx = ur.lse0 + ur.lse_h * h + qrow;
-  const float l2 = qrow < nq ? p.lse2[sidx] : INFINITY;
-  const float dd = qrow < nq ? p.delta[sidx] : 0.f;
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // operands ready before any tile load is in flight
+    const long kv_stride = (long)p.Hkv * D;
+    const long q_stride = (long)p.Hq * D;
+    const int q0 = qb * kDqRows;
+    if (q0 >= nq) return;  // a packed sequence shorter than the longest; uniform
+    const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);
+    const int qrow = wrow0 + (lane & 31);
+    bf16x8 qf[KS], df[KS];
+    const long qoff = (ur.q0 + qrow) * q_stride + (long)h * D;
+  #pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * g) : bf16x8{};
+      df[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.dout + qoff + 16 * ks + 8 * g) : bf16x8{};
+    }
+    const long sidx = ur.lse0 + ur.lse_h * h + qrow;
+    const float l2 = qrow < nq ? p.lse2[sidx] : INFINITY;
+    const float dd = qrow < nq ? p.delta[sidx] : 0.f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // operands ready before any tile load is in flight
 
-  int kv_end = nk;
-  if (CAUSAL) kv_end = min(nk, q0 + kDqRows);
-  const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
-  const __bf16* src = (grp == 0 ? p.v : p.k) + ur.k0 * kv_stride + (long)hkv * D;
+    int kv_end = nk;
+    if (CAUSAL) kv_end = min(nk, q0 + kDqRows);
+    const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
+    const __bf16* src = (grp == 0 ? p.v : p.k) + ur.k0 * kv_stride + (long)hkv * D;
 
-  // every buffer starts finite (the first dQ step multiplies zeros by K)
-  for (int i = tid; i < 4 * kDqTile * kRowElems / 8; i += kBwPpThreads)
-    reinterpret_cast<u32x4*>(&k_t[0][0])[i] = u32x4{};
-  for (int i = tid; i < 2 * kDqTile * kRowElems / 8; i += kBwPpThreads)
-    reinterpret_cast<u32x4*>(&v_t[0][0])[i] = u32x4{};
-  __syncthreads();
+    // every buffer starts finite (the first dQ step multiplies zeros by K)
+    for (int i = tid; i < 4 * kDqTile * kRowElems / 8; i += kBwPpThreads)
+      reinterpret_cast<u32x4*>(&k_t[0][0])[i] = u32x4{};
+    for (int i = tid; i < 2 * kDqTile * kRowElems / 8; i += kBwPpThreads)
+      reinterpret_cast<u32x4*>(&v_t[0][0])[i] = u32x4{};
+    __syncthreads();
 
-  TileCopy<kDqTile, D> stage;
-  auto fetch = [&](int j) {
-    const int j0 = j * kDqTile;
-    stage.load(src + (long)j0 * kv_stride, kv_stride, min(kv_end - j0, kDqTile), gtid);
-  };
-  auto kbuf = [&](auto I) -> __bf16* { return k_t[decltype(I)::value & 3]; };
-  auto vbuf = [&](auto I) -> __bf16* { return v_t[decltype(I)::value & 1]; };
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  f32x16 acc[TD];
-#pragma unroll
-  for (int t = 0; t < TD; ++t) acc[t] = f32x16{};
-  f32x16 s_acc = {}, dp_acc = {};
-  u32x4 ds_pk[2] = {};
-
-  // MFMA phase slices: 0 .. 2 KS - 1 are S and dP of tile j, alternating (one
-  // K or V row operand each), then 2 TD slices of dQ of tile j-1 (one K^T
-  // operand each).  Each slice's LDS operand is read kAhead slices before its
-  // MFMA; scheduling barriers between the slices keep that order.  The tile
-  // move sits after slice kMoveAt, half-way.
-  constexpr int kSD = 2 * KS;
-  constexpr int kSlices = kSD + 2 * TD, kAhead = 4, kMoveAt = kSlices / 2;
-  auto period = [&](int j, auto J) {
-    constexpr int j4 = decltype(J)::value;  // j % 4
-    const __bf16* kt = kbuf(std::integral_constant<int, j4>{});
-    const __bf16* vt = vbuf(std::integral_constant<int, j4>{});
-    const __bf16* kto = kbuf(std::integral_constant<int, j4 + 3>{});  // tile j-1
-    auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
-      constexpr int i = decltype(I)::value;
-      if constexpr (i < kSD) return L::read_rows((i & 1) ? vt : kt, 0, i >> 1, lane);
-      else return L::read_cols(kto, 16 * ((i - kSD) / TD), 32 * ((i - kSD) % TD), lane);
+    TileCopy<kDqTile, D> stage;
+    auto fetch = [&](int j) {
+      const int j0 = j * kDqTile;
+      stage.load(src + (long)j0 * kv_stride, kv_stride, min(kv_end - j0, kDqTile), gtid);
     };
-    // ---- MFMA phase, with this group's tile move after slice kMoveAt
-    bf16x8 opnd[kAhead];
-    static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
-      opnd[decltype(I)::value] = operand(I);
-    });
-    static_for<0, kSlices>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = decltype(I)::value;
-      const bf16x8 a = opnd[i % kAhead];
-      if constexpr (i + kAhead < kSlices) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
-      if constexpr (i < kSD) {
-        constexpr int ks = i >> 1;
-        if constexpr (i & 1)
-          dp_acc = mfma32(a, df[ks], ks == 0 ? f32x16{} : dp_acc);
-        else
-          s_acc = mfma32(a, qf[ks], ks == 0 ? f32x16{} : s_acc);
-      } else {
-        constexpr int hh = (i - kSD) / TD, t = (i - kSD) % TD;
-        acc[t] = mfma32(a, __builtin_bit_cast(bf16x8, ds_pk[hh]), acc[t]);
-      }
+    auto kbuf = [&](auto I) -> __bf16* { return k_t[decltype(I)::value & 3]; };
+    auto vbuf = [&](auto I) -> __bf16* { return v_t[decltype(I)::value & 1]; };
+    auto barrier = [&]() {
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i == kMoveAt) {
-        // group 0 stores V_{j+1} over V_{j-1}, group 1 K_{j+1} over K_{j-3}
-        if (j + 1 < n_tiles) {
-          stage.store(grp == 0 ? vbuf(std::integral_constant<int, j4 + 1>{})
-                               : kbuf(std::integral_constant<int, j4 + 1>{}),
-                      gtid);
-          if (j + 2 < n_tiles) fetch(j + 2);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    f32x16 acc[TD];
+  #pragma unroll
+    for (int t = 0; t < TD; ++t) acc[t] = f32x16{};
+    f32x16 s_acc = {}, dp_acc = {};
+    u32x4 ds_pk[2] = {};
+
+    // MFMA phase slices: 0 .. 2 KS - 1 are S and dP of tile j, alternating (one
+    // K or V row operand each), then 2 TD slices of dQ of tile j-1 (one K^T
+    // operand each).  Each slice's LDS operand is read kAhead slices before its
+    // MFMA; scheduling barriers between the slices keep that order.  The tile
+    // move sits after slice kMoveAt, half-way.
+    constexpr int kSD = 2 * KS;
+    constexpr int kSlices = kSD + 2 * TD, kAhead = 4, kMoveAt = kSlices / 2;
+    auto period = [&](int j, auto J) {
+      constexpr int j4 = decltype(J)::value;  // j % 4
+      const __bf16* kt = kbuf(std::integral_constant<int, j4>{});
+      const __bf16* vt = vbuf(std::integral_constant<int, j4>{});
+      const __bf16* kto = kbuf(std::integral_constant<int, j4 + 3>{});  // tile j-1
+      auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < kSD) return L::read_rows((i & 1) ? vt : kt, 0, i >> 1, lane);
+        else return L::read_cols(kto, 16 * ((i - kSD) / TD), 32 * ((i - kSD) % TD), lane);
+      };
+      // ---- MFMA phase, with this group's tile move after slice kMoveAt
+      bf16x8 opnd[kAhead];
+      static_for<0, kAhead>([&](auto I) __attribute__((always_inline)) {
+        opnd[decltype(I)::value] = operand(I);
+      });
+      static_for<0, kSlices>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        const bf16x8 a = opnd[i % kAhead];
+        if constexpr (i + kAhead < kSlices) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
+        if constexpr (i < kSD) {
+          constexpr int ks = i >> 1;
+          if constexpr (i & 1)
+            dp_acc = mfma32(a, df[ks], ks == 0 ? f32x16{} : dp_acc);
+          else
+            s_acc = mfma32(a, qf[ks], ks == 0 ? f32x16{} : s_acc);
+        } else {
+          constexpr int hh = (i - kSD) / TD, t = (i - kSD) % TD;
+          acc[t] = mfma32(a, __builtin_bit_cast(bf16x8, ds_pk[hh]), acc[t]);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
-    });
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    barrier();
-    // ---- VALU phase: P, dS of tile j (zero past the last tile).  A tile whose
-    // keys all are visible to all of this wave's rows skips the mask.
-    if (j < n_tiles) {
-      const int j0 = j * kDqTile;
-      const bool full = j0 + kDqTile <= nk && (!CAUSAL || j0 + kDqTile - 1 <= wrow0);
-      auto dsval = [&](int r, bool masked) __attribute__((always_inline)) {
-        const int kk = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool vis = !masked || (kk < nk && (!CAUSAL || kk <= qrow));
-        const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -l2)) : 0.f;
-        return pe * (dp_acc[r] - dd);
-      };
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const bf16x2 pk = {(__bf16)dsval(r, false), (__bf16)dsval(r + 1, false)};
-          ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+        if constexpr (i == kMoveAt) {
+          // group 0 stores V_{j+1} over V_{j-1}, group 1 K_{j+1} over K_{j-3}
+          if (j + 1 < n_tiles) {
+            stage.store(grp == 0 ? vbuf(std::integral_constant<int, j4 + 1>{})
+                                 : kbuf(std::integral_constant<int, j4 + 1>{}),
+                        gtid);
+            if (j + 2 < n_tiles) fetch(j + 2);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      // ---- VALU phase: P, dS of tile j (zero past the last tile).  A tile whose
+      // keys all are visible to all of this wave's rows skips the mask.
+      if (j < n_tiles) {
+        const int j0 = j * kDqTile;
+        const bool full = j0 + kDqTile <= nk && (!CAUSAL || j0 + kDqTile - 1 <= wrow0);
+        auto dsval = [&](int r, bool masked) __attribute__((always_inline)) {
+          const int kk = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = !masked || (kk < nk && (!CAUSAL || kk <= qrow));
+          const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -l2)) : 0.f;
+          return pe * (dp_acc[r] - dd);
+        };
+        if (full) {
+  #pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const bf16x2 pk = {(__bf16)dsval(r, false), (__bf16)dsval(r + 1, false)};
+            ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+          }
+        } else {
+  #pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const bf16x2 pk = {(__bf16)dsval(r, true), (__bf16)dsval(r + 1, true)};
+            ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+          }
         }
       } else {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const bf16x2 pk = {(__bf16)dsval(r, true), (__bf16)dsval(r + 1, true)};
-          ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
-        }
+        ds_pk[0] = ds_pk[1] = u32x4{};
       }
-    } else {
-      ds_pk[0] = ds_pk[1] = u32x4{};
+      barrier();
+    };
+
+    if (n_tiles > 0) {
+      fetch(0);
+      stage.store(grp == 0 ? v_t[0] : k_t[0], gtid);
     }
-    barrier();
-  };
+    if (n_tiles > 1) fetch(1);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __syncthreads();
+    if (grp == 1) barrier();  // group 1 runs half a period behind
+    int j = 0;
+    for (; j + 3 <= n_tiles; j += 4) {
+      period(j, std::integral_constant<int, 0>{});
+      period(j + 1, std::integral_constant<int, 1>{});
+      period(j + 2, std::integral_constant<int, 2>{});
+      period(j + 3, std::integral_constant<int, 3>{});
+    }
+    if (j <= n_tiles) period(j, std::integral_constant<int, 0>{});
+    if (j + 1 <= n_tiles) period(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 <= n_tiles) period(j + 2, std::integral_constant<int, 2>{});
+    if (grp == 0) barrier();
 
-  if (n_tiles > 0) {
-    fetch(0);
-    stage.store(grp == 0 ? v_t[0] : k_t[0], gtid);
-  }
-  if (n_tiles > 1) fetch(1);
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __syncthreads();
-  if (grp == 1) barrier();  // group 1 runs half a period behind
-  int j = 0;
-  for (; j + 3 <= n_tiles; j += 4) {
-    period(j, std::integral_constant<int, 0>{});
-    period(j + 1, std::integral_constant<int, 1>{});
-    period(j + 2, std::integral_constant<int, 2>{});
-    period(j + 3, std::integral_constant<int, 3>{});
-  }
-  if (j <= n_tiles) period(j, std::integral_constant<int, 0>{});
-  if (j + 1 <= n_tiles) period(j + 1, std::integral_constant<int, 1>{});
-  if (j + 2 <= n_tiles) period(j + 2, std::integral_constant<int, 2>{});
-  if (grp == 0) barrier();
-
-  if (qrow < nq) {
-    __bf16* row = p.dq + qoff;
-#pragma unroll
-    for (int t = 0; t < TD; ++t)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[t][4 * r4 + e] * p.scale);
-        *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * r4 + 4 * g) = a;
-      }
-  }
+    if (qrow < nq) {
+      __bf16* row = p.dq + qoff;
+  #pragma unroll
+      for (int t = 0; t < TD; ++t)
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 a;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[t][4 * r4 + e] * p.scale);
+          *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * r4 + 4 * g) = a;
+        }
+    }
+  });
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0; }
@@ -748,6 +773,9 @@ int launch_backward_d(BwdParams p, const __bf16* o, const float* lse, int pre_b,
   if (grid_k > INT_MAX || grid_q > INT_MAX || grid_pre > INT_MAX) return ATTN_ERR_TOO_LARGE;
   float* lse2 = const_cast<float*>(p.lse2);
   float* delta = const_cast<float*>(p.delta);
+  // Paired items (run_items) everywhere but the packed form, where the
+  // sequences' differing lengths make pairs uneven (measured 1 % slower).
+  const bool packed = p.cu_q != nullptr;
   if (need_q) {
     hipLaunchKernelGGL(bwd_preprocess<D>, dim3((unsigned)grid_pre), dim3(256), 0, st, o, p.dout,
                        lse, lse2, delta, pre_b, p.Hq, (int)pre_nq, lse_rows);
@@ -755,22 +783,22 @@ int launch_backward_d(BwdParams p, const __bf16* o, const float* lse, int pre_b,
   }
   if (need_k) {
     p.nblk = nblk_k;
+    p.paired = packed ? 0 : nblk_k % 2 == 0;
+    const unsigned wgs = (unsigned)(p.paired ? grid_k / 2 : grid_k);
     if (causal)
-      hipLaunchKernelGGL((bwd_dkdv_pp_kernel<D, true>), dim3((unsigned)grid_k), dim3(kBwPpThreads),
-                         0, st, p);
+      hipLaunchKernelGGL((bwd_dkdv_pp_kernel<D, true>), dim3(wgs), dim3(kBwPpThreads), 0, st, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_pp_kernel<D, false>), dim3((unsigned)grid_k), dim3(kBwPpThreads),
-                         0, st, p);
+      hipLaunchKernelGGL((bwd_dkdv_pp_kernel<D, false>), dim3(wgs), dim3(kBwPpThreads), 0, st, p);
     if (int rc = launched()) return rc;
   }
   if (need_q) {
     p.nblk = nblk_q;
+    p.paired = packed ? 0 : (nblk_q * p.G) % 2 == 0;
+    const unsigned wgs = (unsigned)(p.paired ? grid_q / 2 : grid_q);
     if (causal)
-      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, true>), dim3((unsigned)grid_q), dim3(kBwPpThreads),
-                         0, st, p);
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, true>), dim3(wgs), dim3(kBwPpThreads), 0, st, p);
     else
-      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, false>), dim3((unsigned)grid_q), dim3(kBwPpThreads),
-                         0, st, p);
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<D, false>), dim3(wgs), dim3(kBwPpThreads), 0, st, p);
     if (int rc = launched()) return rc;
   }
   return ATTN_OK;
