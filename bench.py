@@ -47,10 +47,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_18_amd", "csrc", n) for n in ("attn_fwd.hip", "cdna4.h")]
 
 
+def _code_tokens(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed to one space."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, copied whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha256() -> str:
+    """sha256 of the forward's code (attn_fwd.hip, then cdna4.h), comments and layout ignored."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        h.update(open(path, "rb").read())
+        h.update(_code_tokens(open(path, encoding="utf-8").read()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 
@@ -58,9 +84,9 @@ def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 summary of this workload.
 
     The summary records FETCH_SIZE / WRITE_SIZE of the forward scaled by a
-    plain-copy calibration, and the sha256 of the forward's sources
-    (attn_fwd.hip, then cdna4.h) it was taken on; a summary of another
-    kernel version gives None.
+    plain-copy calibration, and the sha256 of the forward's code (attn_fwd.hip,
+    then cdna4.h, comments and whitespace ignored) it was taken on; a summary
+    of other code gives None.
     """
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}.md")
     if not os.path.exists(path):

@@ -69,7 +69,9 @@
 //   the CDNA form of the ping-pong of FlashAttention-4 (papercache summary),
 //   section 3.1.2.  One workgroup barrier per half period.  K/V tiles move
 //   global -> VGPRs -> LDS (16-byte loads, one tile per group per period,
-//   double-buffered), the LDS stores spread over the MFMA phase.
+//   double-buffered), the LDS stores spread over the MFMA phase.  Outside
+//   the block-sparse form a workgroup runs two query blocks of one unit, the
+//   i-th longest and the i-th shortest, back to back.
 // * d = 64: attn_fwd_kernel, 4 waves / 128 query rows per workgroup, each
 //   wave interleaving its own softmax with its MFMAs slice by slice; K/V tiles
 //   move global -> LDS directly (buffer_load ... lds), K two tiles ahead.
@@ -1057,8 +1059,9 @@ int dispatch(const Params& p, int d, bool causal, bool varlen, int grid, hipStre
                 : launch_one<128, false, false>(p, grid, stream);
 }
 
-// Workgroups for `units` (batch, KV head) units of `per_unit` items each,
-// units padded to a multiple of the XCD count (decode_work).
+// Work items for `units` (batch, KV head) units of `per_unit` items each,
+// units padded to a multiple of the XCD count (decode_work); a ping-pong
+// launch runs two items per workgroup (pp_grid).
 long grid_size(long units, long per_unit) { return (units + kXcds - 1) / kXcds * kXcds * per_unit; }
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
