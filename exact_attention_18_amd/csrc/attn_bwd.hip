@@ -773,9 +773,10 @@ int launch_backward_d(BwdParams p, const __bf16* o, const float* lse, int pre_b,
   if (grid_k > INT_MAX || grid_q > INT_MAX || grid_pre > INT_MAX) return ATTN_ERR_TOO_LARGE;
   float* lse2 = const_cast<float*>(p.lse2);
   float* delta = const_cast<float*>(p.delta);
-  // Paired items (run_items) everywhere but the packed form, where the
-  // sequences' differing lengths make pairs uneven (measured 1 % slower).
-  const bool packed = p.cu_q != nullptr;
+  // Paired items (run_items) for the batched form with at most 8192 keys,
+  // as in the forward: the packed form's differing lengths make pairs uneven
+  // (measured 1 % slower), and longer sequences gained nothing.
+  const bool packed = p.cu_q != nullptr || p.Nk > 8192;
   if (need_q) {
     hipLaunchKernelGGL(bwd_preprocess<D>, dim3((unsigned)grid_pre), dim3(256), 0, st, o, p.dout,
                        lse, lse2, delta, pre_b, p.Hq, (int)pre_nq, lse_rows);

@@ -1014,14 +1014,20 @@ constexpr bool use_pp(int d) { return d == 128; }
 // serves 256 rows.
 constexpr int pp_pack(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
 
-// Ping-pong launches pair the items of a unit when a unit has an even count,
-// except block-sparse ones, whose item costs follow the mask rather than the
-// diagonal (pairing measured 2 % slower there).  Returns the workgroups to
-// launch and sets p.items and p.paired.
+// Ping-pong launches pair the items of a unit when a unit has an even count
+// and keys number at most kPairMaxKeys; not block-sparse ones, whose item
+// costs follow the mask rather than the diagonal (pairing measured 2 % slower
+// there).  Longer sequences gain nothing from pairs (an item's launch gap is
+// a small share of it) and lose L2 reuse: a pair's short item streams the
+// start of the key range while the XCD's other workgroups are further on
+// (N = 32768: 8.1 instead of 4.7 GB of HBM traffic).  Returns the workgroups
+// to launch and sets p.items and p.paired.
+constexpr int kPairMaxKeys = 8192;
+
 int pp_grid(Params& p, long items, bool pair) {
   p.items = static_cast<int>(items);
   const int n = p.nqb * (p.G / p.pack);
-  p.paired = (pair && n % 2 == 0) ? 1 : 0;
+  p.paired = (pair && p.Nk <= kPairMaxKeys && n % 2 == 0) ? 1 : 0;
   return static_cast<int>(p.paired ? items / 2 : items);
 }
 
