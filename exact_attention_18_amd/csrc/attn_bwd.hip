@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
     const int key = wk0 + (lane & 31);
     f32x16 dk_acc[TD], dv_acc[TD];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < TD; ++t) dk_acc[t] = dv_acc[t] = f32x16{};
 
     const int s0 = CAUSAL ? (k0 / kQStep) : 0;
@@ -434,13 +434,13 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
         const float* ddt = st_t[grp][B0] + kQStep;
         const bool full = wk0 + 32 <= nk && (!CAUSAL || wk0 + 31 <= i0);
         auto block = [&](bool masked) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int qi = 8 * r4 + 4 * g;
             const float4 l2 = *reinterpret_cast<const float4*>(l2t + qi);
             const float4 dd = *reinterpret_cast<const float4*>(ddt + qi);
             float pv[4], dsv[4];
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * r4 + e;
               const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
@@ -493,9 +493,9 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     float* red = reinterpret_cast<float*>(kv_t);  // K and V are no longer needed
     const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
     auto xfer = [&](f32x16* acc, bool add) {
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < TD; ++t)
-  #pragma unroll
+#pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g);
           if (add) {
@@ -521,12 +521,12 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     if (grp == 0 && key < ur.k_write && key < k0 + kKeysPerWg) {
       __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * D;
       __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * D;
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < TD; ++t)
-  #pragma unroll
+#pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           bf16x4 a, c;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             a[e] = (__bf16)(dk_acc[t][4 * r4 + e] * p.scale);
             c[e] = (__bf16)dv_acc[t][4 * r4 + e];
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     const int qrow = wrow0 + (lane & 31);
     bf16x8 qf[KS], df[KS];
     const long qoff = (ur.q0 + qrow) * q_stride + (long)h * D;
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.q + qoff + 16 * ks + 8 * g) : bf16x8{};
       df[ks] = qrow < nq ? *reinterpret_cast<const bf16x8*>(p.dout + qoff + 16 * ks + 8 * g) : bf16x8{};
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     };
 
     f32x16 acc[TD];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < TD; ++t) acc[t] = f32x16{};
     f32x16 s_acc = {}, dp_acc = {};
     u32x4 ds_pk[2] = {};
@@ -693,13 +693,13 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
           return pe * (dp_acc[r] - dd);
         };
         if (full) {
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const bf16x2 pk = {(__bf16)dsval(r, false), (__bf16)dsval(r + 1, false)};
             ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
           }
         } else {
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const bf16x2 pk = {(__bf16)dsval(r, true), (__bf16)dsval(r + 1, true)};
             ds_pk[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
@@ -733,12 +733,12 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
 
     if (qrow < nq) {
       __bf16* row = p.dq + qoff;
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < TD; ++t)
-  #pragma unroll
+#pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           bf16x4 a;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[t][4 * r4 + e] * p.scale);
           *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * r4 + 4 * g) = a;
         }

@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     const int wrow0 = q0 + (chunk % cph) * kRowsPerWave;
     const int qrow = wrow0 + l32;
     bf16x8 qf[T::KS];
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
       qf[ks] = qrow < q_len
                    ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     const int nch = fetch_v ? CHV : CHK;  // chunks per lane of this group's tiles
     const uint32_t row_bytes = static_cast<uint32_t>(fetch_v ? v_stride : k_stride) * 2u;
     uint32_t goff[CH];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = (i * 4 + gw) * 64 + lane;
       int row, colb;
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<__bf16*>(gbase + (long)kv0 * (row_bytes / 2)), (short)0, nrows * (int)row_bytes,
           kBufferFlags);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < CH; ++i)
         if (i < nch)
           stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, goff[i], 0, 0));
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
     };
     auto store_tile = [&](__bf16* dst) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < CH; ++i)
         if (i < nch) *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
     };
@@ -730,9 +730,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     f32x16 sv[T::KT];
     u32x4 pv_op[T::KT][2];
     f32x16 acc[TV::DT];
-  #pragma unroll
+#pragma unroll
     for (int dt = 0; dt < TV::DT; ++dt) acc[dt] = f32x16{};
-  #pragma unroll
+#pragma unroll
     for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -790,9 +790,9 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     auto apply_mask = [&](int tile) __attribute__((always_inline)) {
       const int kv0 = tile * T::BC;
       const bool bvis = block_visible(tile);
-  #pragma unroll
+#pragma unroll
       for (int kt = 0; kt < T::KT; ++kt)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           const bool vis = bvis && key < nk && (!CAUSAL || key <= qrow);
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       const int tile = tile_of(j);
       if (needs_mask(tile)) apply_mask(tile);
       float m0 = -INFINITY, m1 = -INFINITY;
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < 32; e += 4) {
         m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
         m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
@@ -819,13 +819,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         m_run = m_new;
         m_use = (m_new == -INFINITY) ? 0.f : m_new;
         l_run *= alpha;
-  #pragma unroll
+#pragma unroll
         for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
       }
       float ls0 = 0.f, ls1 = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int kt = 0; kt < T::KT; ++kt)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], c, -m_use));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       barrier();
     };
 
-  #pragma unroll
+#pragma unroll
     for (int kt = 0; kt < T::KT; ++kt) pv_op[kt][0] = pv_op[kt][1] = u32x4{};
     for (int i = tid; i < TV::V_ELEMS / 8; i += kPpThreads)
       reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
@@ -923,12 +923,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     if (qrow < q_len) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       __bf16* orow = p.o + (q_row0 + qrow) * o_stride + (long)h * DV;
-  #pragma unroll
+#pragma unroll
       for (int dt = 0; dt < TV::DT; ++dt)
-  #pragma unroll
+#pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           bf16x4 ov;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
           *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * rq + 4 * g) = ov;
         }
