@@ -27,7 +27,8 @@
 //   (papercache summary), section 3.2.2: iterate along the KV sequence,
 //   values transposed relative to the forward.
 // * bwd_dq_pp_kernel: one workgroup of 8 waves per 256 query rows of one
-//   head, the forward's orientation (S^T = K Q^T, one query per lane), with
+//   head (or 256 / P rows of each of P query heads of one KV group), the
+//   forward's orientation (S^T = K Q^T, one query per lane), with
 //   dP^T = V dO^T, dS^T = P^T * (dP^T - D) and dQ^T += K^T dS^T over key
 //   tiles of 32.  The two wave groups alternate MFMA and VALU phases half a
 //   period apart, as the forward does.  dQ is summed over all key tiles
@@ -77,6 +78,7 @@ struct BwdParams {
   long Tq;                    // packed form: total query rows (the LSE row stride per head)
   int nblk;             // key blocks (dK/dV) or query blocks (dQ) per (batch, head)
   int paired;           // 1: a workgroup runs the i-th and (n-1-i)-th item of a unit of n
+  int pack;             // dQ: query heads of one KV group per workgroup (1, 2, 4 or 8)
   float c;              // scale * log2(e)
   float scale;
 };
@@ -568,25 +570,34 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   const int gtid = tid & (kBwThreads - 1);
   const int g = lane >> 5;
 
-  run_items(p, p.nblk * p.G, [&](const int id) __attribute__((always_inline)) {
+  run_items(p, p.nblk * (p.G / p.pack), [&](const int id) __attribute__((always_inline)) {
     const int units = p.B * p.Hkv;
-    const int per_unit = p.nblk * p.G;
+    // The workgroup takes P = p.pack query heads of the KV group, 256 / P rows
+    // of each: row chunk c = 2 (w % 4) + w / 4 of wave w holds rows
+    // (c % cph) * 32 .. +31 of head gi + c / cph, so the two waves of a SIMD
+    // share their causal extent, and under the causal mask the workgroup's
+    // rows cross fewer key tiles on the diagonal (as in the forward).
+    const int per_unit = p.nblk * (p.G / p.pack);
     const int x = id % kXcds, rr = id / kXcds;
     const int u = (rr / per_unit) * kXcds + x;
     if (u >= units) return;
     const int item = rr % per_unit;
-    const int qbi = item / p.G, gi = item % p.G;
+    const int groups = p.G / p.pack;
+    const int qbi = item / groups, gi = (item % groups) * p.pack;
     const int qb = CAUSAL ? (p.nblk - 1 - qbi) : qbi;
     const int b = u / p.Hkv, hkv = u % p.Hkv;
-    const int h = hkv * p.G + gi;
+    const int chunk = 2 * (wave & 3) + grp;
+    const int cph = 8 / p.pack;                 // 32-row chunks per head
+    const int rows_h = 32 * cph;                // query rows per head
+    const int h = hkv * p.G + gi + chunk / cph;
     const UnitRows ur = unit_rows(p, b);
     const int nk = ur.nk, nq = ur.nq;
 
     const long kv_stride = (long)p.Hkv * D;
     const long q_stride = (long)p.Hq * D;
-    const int q0 = qb * kDqRows;
+    const int q0 = qb * rows_h;
     if (q0 >= nq) return;  // a packed sequence shorter than the longest; uniform
-    const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);
+    const int wrow0 = q0 + 32 * (chunk % cph);
     const int qrow = wrow0 + (lane & 31);
     bf16x8 qf[KS], df[KS];
     const long qoff = (ur.q0 + qrow) * q_stride + (long)h * D;
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // operands ready before any tile load is in flight
 
     int kv_end = nk;
-    if (CAUSAL) kv_end = min(nk, q0 + kDqRows);
+    if (CAUSAL) kv_end = min(nk, q0 + rows_h);
     const int n_tiles = (kv_end + kDqTile - 1) / kDqTile;
     const __bf16* src = (grp == 0 ? p.v : p.k) + ur.k0 * kv_stride + (long)hkv * D;
 
@@ -766,8 +777,12 @@ int launch_backward_d(BwdParams p, const __bf16* o, const float* lse, int pre_b,
   constexpr long kPreRows = 256 / (D / 8);  // rows per preprocess block
   const long units8 = ((long)p.B * p.Hkv + kXcds - 1) / kXcds * kXcds;
   const int nblk_k = (p.Nk + kKeysPerWg - 1) / kKeysPerWg;
-  const int nblk_q = (p.Nq + kDqRows - 1) / kDqRows;
-  const long grid_k = units8 * nblk_k, grid_q = units8 * nblk_q * p.G;
+  // dQ workgroups take the largest power of two up to 8 dividing G of a KV
+  // group's query heads together (256 / pack rows of each).
+  p.pack = p.G % 8 == 0 ? 8 : p.G % 4 == 0 ? 4 : p.G % 2 == 0 ? 2 : 1;
+  const int rows_q = kDqRows / p.pack;
+  const int nblk_q = (p.Nq + rows_q - 1) / rows_q;
+  const long grid_k = units8 * nblk_k, grid_q = units8 * nblk_q * (p.G / p.pack);
   const long rows = (long)pre_b * pre_nq * p.Hq;
   const long grid_pre = (rows + kPreRows - 1) / kPreRows;
   if (grid_k > INT_MAX || grid_q > INT_MAX || grid_pre > INT_MAX) return ATTN_ERR_TOO_LARGE;
@@ -794,7 +809,7 @@ int launch_backward_d(BwdParams p, const __bf16* o, const float* lse, int pre_b,
   }
   if (need_q) {
     p.nblk = nblk_q;
-    p.paired = packed ? 0 : (nblk_q * p.G) % 2 == 0;
+    p.paired = packed ? 0 : (nblk_q * (p.G / p.pack)) % 2 == 0;
     const unsigned wgs = (unsigned)(p.paired ? grid_q / 2 : grid_q);
     if (causal)
       hipLaunchKernelGGL((bwd_dq_pp_kernel<D, true>), dim3(wgs), dim3(kBwPpThreads), 0, st, p);
