@@ -80,7 +80,7 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, profiles_dir: str = os.path.join(ROOT, "profiles")):
     """HBM bytes per launch from the committed rocprofv3 summary of this workload.
 
     The summary records FETCH_SIZE / WRITE_SIZE of the forward scaled by a
@@ -88,7 +88,7 @@ def measured_traffic(workload: str):
     then cdna4.h, comments and whitespace ignored) it was taken on; a summary
     of other code gives None.
     """
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}.md")
+    path = os.path.join(profiles_dir, f"attn_fwd_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}

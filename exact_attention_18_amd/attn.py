@@ -10,6 +10,7 @@ returns an error, a ``RuntimeError`` is raised.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -19,6 +20,10 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
+# The race-check build: the same kernels with conservative synchronisation
+# (compiled with ATTN_FORCE_SAFE=1); used only to check that the tuned build
+# has no missing wait or barrier.
+SAFE_LIB_PATH = os.path.join(_PKG, "libattn_safe.so")
 
 # attn_status codes (include/attn.h)
 ATTN_OK = 0
@@ -30,9 +35,11 @@ ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
 
-EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen", "attn_varlen_plan",
-           "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_size",
-           "attn_probe_mfma", "attn_strerror", "attn_last_hip_error", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen",
+           "attn_fwd_varlen_ordered", "attn_varlen_plan", "attn_bwd", "attn_bwd_varlen",
+           "attn_bwd_varlen_ordered", "attn_bwd_workspace_size",
+           "attn_probe_mfma", "attn_probe_xcd", "attn_strerror", "attn_last_hip_error",
+           "attn_version")
 
 _lib = None
 
@@ -56,20 +63,28 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          vp, vp, i32, vp]
     lib.attn_fwd_blocksparse.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
-                                    i32, vp, vp]
+                                    i32, vp]
     lib.attn_fwd_varlen.restype = i32
+    lib.attn_fwd_varlen_ordered.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            f32, i32, vp, vp]
+    lib.attn_fwd_varlen_ordered.restype = i32
     lib.attn_varlen_plan.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     lib.attn_varlen_plan.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                              f32, i32, vp, vp]
     lib.attn_bwd.restype = i32
     lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
-                                    i32, i32, i32, i32, f32, i32, vp, vp]
+                                    i32, i32, i32, i32, f32, i32, vp]
     lib.attn_bwd_varlen.restype = i32
+    lib.attn_bwd_varlen_ordered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                            i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_bwd_varlen_ordered.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_probe_mfma.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.attn_probe_mfma.restype = i32
+    lib.attn_probe_xcd.argtypes = [i32, vp, vp]
+    lib.attn_probe_xcd.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -79,6 +94,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if path is None:
         _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route the calls of this module through another build of the library (e.g. SAFE_LIB_PATH)."""
+    global _lib
+    saved = load_library()
+    _lib = load_library(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def strerror(code: int) -> str:
@@ -175,7 +202,9 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
 
     Returns O bf16 [Tq,Hq,d] and LSE fp32 [Hq,Tq].  Rows of a freshly allocated
     O / LSE that belong to no sequence are left as zero.  seq_order (int32 [S],
-    from attn_varlen_plan) sets the order in which sequences are scheduled.
+    from attn_varlen_plan) sets the order in which sequences are scheduled
+    (attn_fwd_varlen_ordered); without it the sequences run in index order
+    (attn_fwd_varlen).
     """
     lib = load_library()
     _need(q, "q", torch.bfloat16)
@@ -211,11 +240,15 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         _need(lse, "lse", torch.float32, dev)
         if lse.shape != (Hq, Tq):
             raise ValueError("lse must have shape [Hq,Tq]")
-    rc = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
-                             _ptr(cu_seqlens_k), num_seqs, Hq, Hkv, int(max_seqlen_q),
-                             int(max_seqlen_k), d, float(scale), int(bool(causal)),
-                             _ptr(seq_order), _stream_handle(dev))
-    _check(rc, "attn_fwd_varlen")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            num_seqs, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
+            int(bool(causal)))
+    if seq_order is None:
+        rc = lib.attn_fwd_varlen(*args, _stream_handle(dev))
+        _check(rc, "attn_fwd_varlen")
+    else:
+        rc = lib.attn_fwd_varlen_ordered(*args, _ptr(seq_order), _stream_handle(dev))
+        _check(rc, "attn_fwd_varlen_ordered")
     return out, lse
 
 
@@ -351,12 +384,15 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
         _need(dv, "dv", torch.bfloat16, dev)
         if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
             raise ValueError("dq, dk, dv must have the shapes of q, k, v")
-    rc = lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                             _ptr(dk), _ptr(dv), _ptr(workspace), _ptr(cu_seqlens_q),
-                             _ptr(cu_seqlens_k), num_seqs, Tq, Hq, Hkv, int(max_seqlen_q),
-                             int(max_seqlen_k), d, float(scale), int(bool(causal)),
-                             _ptr(seq_order), _stream_handle(dev))
-    _check(rc, "attn_bwd_varlen")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, Tq, Hq,
+            Hkv, int(max_seqlen_q), int(max_seqlen_k), d, float(scale), int(bool(causal)))
+    if seq_order is None:
+        rc = lib.attn_bwd_varlen(*args, _stream_handle(dev))
+        _check(rc, "attn_bwd_varlen")
+    else:
+        rc = lib.attn_bwd_varlen_ordered(*args, _ptr(seq_order), _stream_handle(dev))
+        _check(rc, "attn_bwd_varlen_ordered")
     return dq, dk, dv
 
 
@@ -433,3 +469,16 @@ def attn_probe_mfma(operands: torch.Tensor, iters: int, workgroups: int,
 
 def probe_flop(iters: int, workgroups: int) -> float:
     return float(workgroups) * PROBE_WAVES * iters * PROBE_FLOP_PER_ITER
+
+
+def attn_probe_xcd(workgroups: int, device=None) -> torch.Tensor:
+    """Placement of a grid of 512-thread workgroups: int32 [workgroups, 2] on the device.
+
+    Row w holds the XCD workgroup w ran on and the raw HW_ID register of its
+    first wave (attn_probe_xcd in include/attn.h).
+    """
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    ids = torch.empty((workgroups, 2), dtype=torch.int32, device=dev)
+    rc = load_library().attn_probe_xcd(int(workgroups), _ptr(ids), _stream_handle(dev))
+    _check(rc, "attn_probe_xcd")
+    return ids

@@ -22,6 +22,9 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip", "mfma_probe.hip")]
 LIB = os.path.join(PKG, "libattn.so")
+# The race-check variant: the same kernels with conservative synchronisation
+# (ATTN_FORCE_SAFE); its outputs must equal libattn.so's bit for bit.
+SAFE_LIB = os.path.join(PKG, "libattn_safe.so")
 ARCH = "gfx950"
 
 
@@ -45,17 +48,21 @@ def compile_flags(extra=()):
     ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile libattn.so; returns its path.  Raises on compiler failure."""
-    tmp = LIB + ".tmp"
+def _compile(out: str, extra, verbose: bool) -> subprocess.Popen:
+    tmp = out + ".tmp"
     cmd = [hipcc_path(), *compile_flags(extra), "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(out: str, proc: subprocess.Popen, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    text, _ = proc.communicate()
     noise = "is not a recognized feature for this target"
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    msgs = "\n".join(l for l in text.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}) for {os.path.basename(out)}:\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
     # Every symbol must resolve (e.g. host stubs of all kernel instantiations).
@@ -64,7 +71,20 @@ def build(verbose: bool = False, extra=()) -> str:
     except OSError as exc:
         os.remove(tmp)
         raise RuntimeError(f"built library does not load: {exc}") from exc
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra=(), safe: bool = True) -> str:
+    """Compile libattn.so (and, with safe, the race-check libattn_safe.so); returns libattn.so's path.
+
+    The two compiles run side by side.  Raises on compiler failure.
+    """
+    jobs = [(LIB, _compile(LIB, extra, verbose))]
+    if safe:
+        jobs.append((SAFE_LIB, _compile(SAFE_LIB, (*extra, "-DATTN_FORCE_SAFE=1"), verbose)))
+    for out, proc in jobs:
+        _finish(out, proc, verbose)
     return LIB
 
 

@@ -835,28 +835,46 @@ extern "C" size_t attn_bwd_workspace_size(int B, int Hq, int Nq) {
   return (size_t)2 * sizeof(float) * (size_t)B * (size_t)Hq * (size_t)Nq;
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                        void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                        float scale, int causal, const int32_t* seqlens_k, void* stream) {
+namespace {
+
+// Host-side checks of the batched backward, except its workspace pointer.
+// Sets *noop when there is nothing to compute.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+              int Nk, int d, float scale, bool* noop) {
+  *noop = false;
   if (B < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SIZE;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SIZE;
-  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  if (!std::isfinite(scale)) return ATTN_ERR_SIZE;  // any finite scale: P = exp2(s c - lse2)
+  if (B == 0 || (Nq == 0 && Nk == 0)) {
+    *noop = true;
+    return ATTN_OK;
+  }
   const bool need_q = Nq > 0, need_k = Nk > 0;
   if ((need_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) ||
       (need_q && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
-                  dq == nullptr || workspace == nullptr)))
+                  dq == nullptr)))
     return ATTN_ERR_NULL;
   if ((need_q && (!aligned16(q) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-                  !aligned16(workspace) || (reinterpret_cast<uintptr_t>(lse) % 4) != 0)) ||
+                  (reinterpret_cast<uintptr_t>(lse) % 4) != 0)) ||
       (need_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))))
     return ATTN_ERR_ALIGN;
   const long rows = (long)B * Nq * Hq;
   if (rows > INT_MAX || (long)B * Nk * Hkv > INT_MAX || (long)Nq * Hq * d > INT_MAX / 2 ||
       (long)Nk * Hkv * d > INT_MAX / 2)
     return ATTN_ERR_TOO_LARGE;
+  return ATTN_OK;
+}
+
+// Launches the batched backward with the LSE * log2(e) and D rows at `ws`
+// (2 * B * Hq * Nq floats, every one written by the preprocess kernel before
+// it is read).
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int Hq, int Hkv,
+            int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
+            void* stream) {
+  const long rows = (long)B * Nq * Hq;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   BwdParams p{};
@@ -864,10 +882,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.k = static_cast<const __bf16*>(k);
   p.v = static_cast<const __bf16*>(v);
   p.dout = static_cast<const __bf16*>(dout);
-  float* lse2 = static_cast<float*>(workspace);
-  float* delta = lse2 + rows;
-  p.lse2 = lse2;
-  p.delta = delta;
+  p.lse2 = ws;
+  p.delta = ws + rows;
   p.dq = static_cast<__bf16*>(dq);
   p.dk = static_cast<__bf16*>(dk);
   p.dv = static_cast<__bf16*>(dv);
@@ -880,21 +896,36 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.Nk = Nk;
   p.scale = scale;
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  return launch_backward(d, p, static_cast<const __bf16*>(o), lse, B, Nq, nullptr, need_q, need_k,
+  return launch_backward(d, p, static_cast<const __bf16*>(o), lse, B, Nq, nullptr, Nq > 0, Nk > 0,
                          causal != 0, st);
 }
 
+}  // namespace
 
-extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
-                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                               void* workspace, const int32_t* cu_seqlens_q,
-                               const int32_t* cu_seqlens_k, int num_seqs, int total_q, int Hq,
-                               int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
-                               int causal, const int32_t* seq_order, void* stream) {
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        float scale, int causal, const int32_t* seqlens_k, void* stream) {
+  bool noop = false;
+  const int rc = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, &noop);
+  if (rc != ATTN_OK || noop) return rc;
+  if (Nq > 0 && workspace == nullptr) return ATTN_ERR_NULL;
+  if (Nq > 0 && !aligned16(workspace)) return ATTN_ERR_ALIGN;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, Nq,
+                 Nk, d, scale, causal, seqlens_k, stream);
+}
+
+extern "C" int attn_bwd_varlen_ordered(const void* q, const void* k, const void* v,
+                                       const void* o, const float* lse, const void* dout, void* dq,
+                                       void* dk, void* dv, void* workspace,
+                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       int num_seqs, int total_q, int Hq, int Hkv,
+                                       int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                                       int causal, const int32_t* seq_order, void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_SIZE;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SIZE;
+  if (!std::isfinite(scale)) return ATTN_ERR_SIZE;  // any finite scale: P = exp2(s c - lse2)
   if (num_seqs == 0 || (max_seqlen_q == 0 && max_seqlen_k == 0)) return ATTN_OK;
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
   const bool need_q = max_seqlen_q > 0 && total_q > 0, need_k = max_seqlen_k > 0;
@@ -935,4 +966,15 @@ extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, cons
   p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   return launch_backward(d, p, static_cast<const __bf16*>(o), lse, 1, total_q,
                          cu_seqlens_q + num_seqs, need_q, need_k, causal != 0, st);
+}
+
+extern "C" int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               void* workspace, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int num_seqs, int total_q, int Hq,
+                               int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                               int causal, void* stream) {
+  return attn_bwd_varlen_ordered(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens_q,
+                                 cu_seqlens_k, num_seqs, total_q, Hq, Hkv, max_seqlen_q,
+                                 max_seqlen_k, d, scale, causal, nullptr, stream);
 }

@@ -108,6 +108,19 @@ struct Tile {
 
 constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
 
+// Race check.  A library built with -DATTN_FORCE_SAFE=1 keeps every
+// arithmetic step and its order but synchronises conservatively: the two
+// wave groups of the ping-pong kernel run in lockstep instead of half a
+// period apart (every LDS buffer is then written and read in different
+// phases of all waves alike), every LDS store and global load is waited for
+// at once and followed by a workgroup barrier, and the d = 64 kernel waits for
+// its tile DMA before computing.  Its outputs must equal the tuned build's
+// bit for bit; a difference exposes a missing wait or barrier.
+#ifndef ATTN_FORCE_SAFE
+#define ATTN_FORCE_SAFE 0
+#endif
+constexpr bool kForceSafe = ATTN_FORCE_SAFE != 0;
+
 struct Params {
   const __bf16* q;
   const __bf16* k;
@@ -125,7 +138,8 @@ struct Params {
   int paired;  // 1: a ping-pong workgroup runs two items of one unit (the i-th longest and shortest)
   int pack;    // query heads of one KV group per workgroup (1, 2, 4 or 8; 1 unless d = 128)
   int num_seqs;
-  float c;  // scale * log2(e)
+  float c;    // |scale| * log2(e) (log2(e) when scale == 0)
+  int qsign;  // sign of scale: 1, -1 (query fragments negated) or 0 (query fragments zeroed)
   const uint8_t* block_mask;  // block-sparse form: [mask_heads, nbq, nbk] of 128 x 128 blocks
   int mask_heads, nbq, nbk;
 };
@@ -166,6 +180,24 @@ __device__ __forceinline__ WorkItem decode_work(const Params& p, bool causal, in
   w.gi = (item % groups) * p.pack;  // first query head of the group this workgroup takes
   w.qb = causal ? (p.nqb - 1 - qbi) : qbi;
   return w;
+}
+
+// The sign of the scale, applied to the query fragments once per work item.
+// The kernels multiply scores by c = |scale| * log2(e) > 0 and take row maxima
+// of the raw MFMA results, which is right only for a positive factor; with
+// the queries negated the raw results are -<q, k>, and -<q, k> * |scale| is
+// scale * <q, k>.  Negating bf16 is exact and fp32 accumulation rounds
+// symmetrically, so a negative scale gives bitwise the result of -scale on
+// negated queries.  With scale == 0 the queries are zeroed: every visible
+// score is exactly 0 and masked keys stay at -inf for any c > 0.
+template <int N>
+__device__ __forceinline__ void apply_qsign(bf16x8 (&qf)[N], int qsign) {
+  if (qsign > 0) return;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const u32x4 x = __builtin_bit_cast(u32x4, qf[i]);
+    qf[i] = qsign == 0 ? bf16x8{} : __builtin_bit_cast(bf16x8, x ^ 0x80008000u);
+  }
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -233,6 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     qf[ks] = qrow < q_len
                  ? *reinterpret_cast<const bf16x8*>(qbase + qrow * q_stride + ks * 16 + 8 * g)
                  : bf16x8{};
+  apply_qsign(qf, p.qsign);
 
   // Keys this workgroup needs: all visible keys of its rows.
   int kv_end = nk;
@@ -481,6 +514,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     const __bf16* vr = P ? v_lds0 : v_lds1;
     if (j + 2 < n_tiles) issue_tile(kbase, kw, kgoff, false, (j + 2) * T::BC);
     issue_tile(vbase, vw, vgoff, true, j * T::BC);
+    if constexpr (kForceSafe) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     iteration(j, vr, kr, fast_tag);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -489,6 +526,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     const bool P = j & 1;
     if (j + 2 < n_tiles) issue_tile(kbase, P ? k_lds1 : k_lds0, kgoff, false, (j + 2) * T::BC);
     issue_tile(vbase, P ? v_lds1 : v_lds0, vgoff, true, j * T::BC);
+    if constexpr (kForceSafe) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     iteration(j, P ? v_lds0 : v_lds1, P ? k_lds0 : k_lds1, std::false_type{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -624,6 +665,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       qf[ks] = qrow < q_len
                    ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
                    : bf16x8{};
+    apply_qsign(qf, p.qsign);
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // qf ready before any tile load is in flight
     int kv_end = nk;
@@ -856,6 +898,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     };
     auto barrier = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kForceSafe) __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -879,6 +922,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       auto move = [&](auto C) __attribute__((always_inline)) {
         constexpr int c = decltype(C)::value;
         if (c < nch) store_chunk(dst, C);
+        if constexpr (kForceSafe) barrier();
         if constexpr (kLoadInMfmaPhase && c == CH - 1) {
           if (st + 1 < n_iter) load_tile_at(next_tile);
         }
@@ -910,14 +954,14 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
-    if (grp == 1) barrier();  // group 1 starts half a period late
+    if (!kForceSafe && grp == 1) barrier();  // group 1 starts half a period late
     int j = 0;
     for (; j + 1 <= n_iter; j += 2) {
       period(j, std::integral_constant<int, 0>{});
       period(j + 1, std::integral_constant<int, 1>{});
     }
     if (j <= n_iter) period(j, std::integral_constant<int, 0>{});
-    if (grp == 0) barrier();
+    if (!kForceSafe && grp == 0) barrier();
 
     const float l_tot = pair_sum(l_run);
     if (qrow < q_len) {
@@ -1075,8 +1119,16 @@ bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>
 int check_common(int Hq, int Hkv, int d, float scale) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SIZE;
+  if (!std::isfinite(scale)) return ATTN_ERR_SIZE;
   return ATTN_OK;
+}
+
+// Scale into the kernel's form: c = |scale| * log2(e) and the sign, which the
+// kernels fold into the query fragments (apply_qsign).
+void set_scale(Params& p, float scale) {
+  const double a = std::fabs(static_cast<double>(scale));
+  p.c = static_cast<float>((scale == 0.f ? 1.0 : a) * 1.4426950408889634);
+  p.qsign = scale > 0.f ? 1 : scale < 0.f ? -1 : 0;
 }
 
 int check_buffers(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -1119,7 +1171,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   p.nqb = static_cast<int>(nqb);
   p.pack = pack;
   p.num_seqs = B;
-  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  set_scale(p, scale);
   return dispatch(p, d, causal != 0, false, static_cast<int>(grid),
                   static_cast<hipStream_t>(stream));
 }
@@ -1155,7 +1207,7 @@ extern "C" int attn_fwd_dims(const void* q, const void* k, const void* v, void* 
   p.nqb = static_cast<int>(nqb);
   p.pack = pack;
   p.num_seqs = B;
-  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  set_scale(p, scale);
   const unsigned wgs = static_cast<unsigned>(pp_grid(p, grid, true));
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -1205,7 +1257,7 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
   p.nqb = static_cast<int>(nqb);
   p.pack = 1;  // the mask is per 128-row block of one head
   p.num_seqs = B;
-  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  set_scale(p, scale);
   p.block_mask = block_mask;
   p.mask_heads = mask_heads;
   p.nbq = (Nq + kSparseBlock - 1) / kSparseBlock;
@@ -1227,11 +1279,11 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                               int num_seqs, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k,
-                               int d, float scale, int causal, const int32_t* seq_order,
-                               void* stream) {
+extern "C" int attn_fwd_varlen_ordered(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k, int num_seqs, int Hq, int Hkv,
+                                       int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                                       int causal, const int32_t* seq_order, void* stream) {
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_SIZE;
   int rc = check_common(Hq, Hkv, d, scale);
   if (rc != ATTN_OK) return rc;
@@ -1261,9 +1313,17 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
   p.nqb = static_cast<int>(nqb);
   p.pack = pack;
   p.num_seqs = num_seqs;
-  p.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  set_scale(p, scale);
   return dispatch(p, d, causal != 0, true, static_cast<int>(grid),
                   static_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int num_seqs, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                               int d, float scale, int causal, void* stream) {
+  return attn_fwd_varlen_ordered(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, Hq, Hkv,
+                                 max_seqlen_q, max_seqlen_k, d, scale, causal, nullptr, stream);
 }
 
 extern "C" int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -1291,7 +1351,7 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (supported: 64, 128)";
     case ATTN_ERR_HEADS: return "bad head counts (need Hq >= 1, Hkv >= 1, Hq % Hkv == 0)";
-    case ATTN_ERR_SIZE: return "negative size, or scale not finite and positive";
+    case ATTN_ERR_SIZE: return "negative size, or scale not finite";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed (see attn_last_hip_error)";
     case ATTN_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_TOO_LARGE: return "problem too large for 32-bit grid or row indexing";

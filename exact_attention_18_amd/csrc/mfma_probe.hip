@@ -107,7 +107,42 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_probe_kernel(const bf16
   }
 }
 
+// Where the dispatcher places workgroups: thread 0 of workgroup w records the
+// XCD it runs on (hardware register XCC_ID, bits 3:0) and the HW_ID register
+// (SE, CU, SIMD and wave slot of wave 0).  The forward's grid order deals its
+// (batch, KV head) units to the XCDs on the premise that workgroup w runs on
+// XCD w % 8; this records what the hardware does.  Workgroups of 512 threads
+// with the LDS reservation of the probe above, as the forward's.
+__global__ __launch_bounds__(kProbeThreads, 1) void xcd_probe_kernel(int32_t* __restrict__ ids) {
+  __shared__ float reserve[kProbeLdsFloats];
+  if (threadIdx.x == 0) {
+    volatile float* res = reserve;
+    res[0] = 0.f;  // keeps the reservation
+    // s_getreg simm16: register id | offset << 6 | (size - 1) << 11
+    const int xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) + (int)res[0];
+    const int hw = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));
+    ids[2 * (long)blockIdx.x] = xcc;
+    ids[2 * (long)blockIdx.x + 1] = hw;
+  }
+}
+
 }  // namespace
+
+extern "C" int attn_probe_xcd(int workgroups, int32_t* ids, void* stream) {
+  if (ids == nullptr) return ATTN_ERR_NULL;
+  if (workgroups < 1) return ATTN_ERR_SIZE;
+  if ((reinterpret_cast<uintptr_t>(ids) & 7u) != 0) return ATTN_ERR_ALIGN;
+  if (workgroups > INT32_MAX / 2) return ATTN_ERR_TOO_LARGE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(workgroups), dim3(kProbeThreads), 0,
+                     static_cast<hipStream_t>(stream), ids);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    attn_detail::last_hip_error = static_cast<int>(err);
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
 
 extern "C" int attn_probe_mfma(const void* operands, int shape, int iters, int workgroups,
                                float* sink, uint64_t* clocks, void* stream) {

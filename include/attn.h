@@ -68,7 +68,7 @@ enum attn_status {
   ATTN_ERR_NULL = -1,      /* a required pointer is NULL                          */
   ATTN_ERR_HEAD_DIM = -2,  /* d is not 64 or 128                                  */
   ATTN_ERR_HEADS = -3,     /* Hkv < 1, Hq < 1 or Hq % Hkv != 0                     */
-  ATTN_ERR_SIZE = -4,      /* negative size, or scale not finite and > 0          */
+  ATTN_ERR_SIZE = -4,      /* negative size, or scale not finite                  */
   ATTN_ERR_LAUNCH = -5,    /* the HIP launch failed (see attn_last_hip_error)     */
   ATTN_ERR_ALIGN = -6,     /* q, k, v or o not 16-byte aligned, lse not 4-byte    */
   ATTN_ERR_TOO_LARGE = -7  /* grid or index range exceeds what the kernel handles */
@@ -83,7 +83,11 @@ enum attn_status {
  *               LSE = -inf.
  *   Hq, Hkv   : query and key/value head counts (Hq % Hkv == 0).
  *   d         : head dimension, 64 or 128.
- *   scale     : finite, > 0 (the workloads use 1/sqrt(d)).
+ *   scale     : any finite value (the workloads use 1/sqrt(d)).  A negative
+ *               scale is computed exactly as scale' = -scale with every query
+ *               element negated (a sign flip is exact in bf16); scale == 0
+ *               makes every visible key equally likely (O = mean of the
+ *               visible V rows, LSE = ln(#visible)).
  *   causal    : non-zero for the causal mask.
  *   seqlens_k : NULL, or device int32 [B] of valid key counts per batch
  *               element (key padding); shared by all heads.
@@ -138,16 +142,31 @@ int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, f
  * is the batched one with the batch and sequence dimensions flattened
  * (FlashAttention notes (xwysyy), code-structure overview, the "unpadded"
  * interface; FlashAttention-4 (papercache summary), section 3.3, varlen
- * metadata held on the device).
- * seq_order is NULL (sequences in index order) or a device int32 [num_seqs]
- * permutation from attn_varlen_plan: workgroups then take the sequences in
- * that order (out-of-range entries are clamped, never read out of bounds).
- * The order changes only the schedule, never a result.
+ * metadata held on the device).  Workgroups take the sequences in index
+ * order; scale, causal, errors and ownership are as for attn_fwd.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
                     int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
-                    int causal, const int32_t* seq_order, void* stream);
+                    int causal, void* stream);
+
+/*
+ * attn_fwd_varlen with the sequences scheduled in a given order: the
+ * virtual-to-actual batch index map of FlashAttention-4 (papercache summary),
+ * section 3.3, that the LPT preprocessing kernel (attn_varlen_plan) writes
+ * and the attention kernel reads back.
+ *   seq_order : NULL (then this is attn_fwd_varlen) or a device int32
+ *               [num_seqs] permutation, as attn_varlen_plan writes it;
+ *               workgroups take sequence seq_order[v] v-th.  Out-of-range
+ *               entries are clamped, never read out of bounds.
+ * Every other argument is as for attn_fwd_varlen.  The order changes only
+ * the schedule, never a result: outputs are bitwise those of attn_fwd_varlen.
+ */
+int attn_fwd_varlen_ordered(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int num_seqs, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                            int d, float scale, int causal, const int32_t* seq_order,
+                            void* stream);
 
 /*
  * Longest-processing-time-first order of the sequences of a packed batch
@@ -166,7 +185,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  *               lk otherwise (lq, lk: the sequence's lengths clamped to the
  *               max_seqlen bounds); the order among equal keys is
  *               unspecified and does not change any output of the forward.
- * Pass seq_order to attn_fwd_varlen (NULL there means sequence order).
+ * Pass seq_order to attn_fwd_varlen_ordered or attn_bwd_varlen_ordered.
  * num_seqs == 0 is a no-op.  Asynchronous on stream; allocates nothing.
  * Returns an attn_status (ATTN_ERR_NULL for a NULL pointer with num_seqs > 0,
  * ATTN_ERR_SIZE for negative sizes).
@@ -185,7 +204,8 @@ int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, i
  * KV head sums over its G = Hq / Hkv query heads.  Masks, GQA map, layouts
  * and `seqlens_k` are those of attn_fwd; keys past seqlens_k[b] get zero
  * gradient.
- *   q, k, v, seqlens_k, scale, causal : exactly as passed to attn_fwd.
+ *   q, k, v, seqlens_k, scale, causal : exactly as passed to attn_fwd (any
+ *               finite scale).
  *   o, lse    : the forward's outputs for these inputs (bf16 [B,Nq,Hq,d] and
  *               fp32 [B,Hq,Nq], natural log).
  *   dout      : bf16 [B,Nq,Hq,d], gradient of the loss with respect to O.
@@ -213,9 +233,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * back to back as that forward describes (FlashAttention notes (xwysyy),
  * code-structure overview, the "unpadded" interface).
  *   q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
- *   max_seqlen_k, scale, causal, seq_order : as passed to attn_fwd_varlen
- *               (seq_order, from attn_varlen_plan or NULL, changes only the
- *               schedule).
+ *   max_seqlen_k, scale, causal : as passed to attn_fwd_varlen.
  *   total_q   : rows of q, o, dout and dq (at least cu_seqlens_q[num_seqs]).
  *   o, lse    : that forward's outputs: bf16 [total_q, Hq, d] and fp32 LSE
  *               rows of cu_seqlens_q[num_seqs] entries per head, as it writes
@@ -235,7 +253,21 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
                     const void* dout, void* dq, void* dk, void* dv, void* workspace,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
                     int total_q, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int d,
-                    float scale, int causal, const int32_t* seq_order, void* stream);
+                    float scale, int causal, void* stream);
+
+/*
+ * attn_bwd_varlen with the sequences scheduled in the order seq_order (NULL,
+ * or the device int32 [num_seqs] permutation attn_varlen_plan writes; the
+ * batch index map of FlashAttention-4 (papercache summary), section 3.3).
+ * The order changes only the schedule: results are bitwise those of
+ * attn_bwd_varlen.  Every other argument is as for attn_bwd_varlen.
+ */
+int attn_bwd_varlen_ordered(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* workspace, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int num_seqs, int total_q, int Hq,
+                            int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                            int causal, const int32_t* seq_order, void* stream);
 
 /* Bytes of workspace attn_bwd needs: two fp32 per (batch, query head, query
  * row); 0 when any argument is <= 0. */
@@ -277,6 +309,24 @@ const char* attn_strerror(int status);
  */
 int attn_probe_mfma(const void* operands, int shape, int iters, int workgroups, float* sink,
                     uint64_t* clocks, void* stream);
+
+/*
+ * Workgroup placement probe (a measurement aid; it computes nothing of the
+ * attention).  The grid order of the forward keeps the key/value tiles of a
+ * (batch, KV head) unit in one XCD's L2 by dealing units round-robin to the
+ * XCDs, which the heads-in-L2-sections scheduling of FlashAttention-4
+ * (papercache summary), section 3.3, calls for; that rests on the dispatcher
+ * placing workgroup w on XCD w % 8.  This call records where each workgroup of
+ * a grid of 512-thread workgroups (the forward's size, one per CU) runs.
+ *   workgroups : >= 1.
+ *   ids        : device int32 [workgroups][2], 8-byte aligned, written:
+ *                ids[w][0] = the XCD (hardware register XCC_ID, 0..7) and
+ *                ids[w][1] = the raw HW_ID register of the workgroup's first
+ *                wave (shader engine, CU, SIMD, wave slot).
+ * Returns ATTN_ERR_NULL, ATTN_ERR_SIZE, ATTN_ERR_ALIGN, ATTN_ERR_TOO_LARGE or
+ * ATTN_ERR_LAUNCH; asynchronous on stream.
+ */
+int attn_probe_xcd(int workgroups, int32_t* ids, void* stream);
 
 /* hipError_t of the last failed launch on this thread (0 if none). */
 int attn_last_hip_error(void);

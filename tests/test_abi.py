@@ -28,6 +28,51 @@ def test_header_declares_the_binding_exports():
     assert _declared_functions() == set(attn.EXPORTS)
 
 
+def _prototypes():
+    """name -> list of (type, name) parameters, from the header's declarations."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b[a-z_][a-z0-9_ ]*[ *]+([a-z_][a-z0-9_]*)\s*\(([^;{]*?)\)\s*;", text):
+        params = [" ".join(p.split()) for p in m.group(2).split(",")]
+        out[m.group(1)] = [] if params == ["void"] else params
+    return out
+
+
+# The primary call and its varlen sibling as the boundary contract states them
+# (the stream is a hipStream_t passed as void*, so the header needs no HIP include).
+CONTRACT = {
+    "attn_fwd": "const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, "
+                "int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k, "
+                "void* stream",
+    "attn_fwd_varlen": "const void* q, const void* k, const void* v, void* o, float* lse, "
+                       "const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs, "
+                       "int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale, "
+                       "int causal, void* stream",
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONTRACT))
+def test_boundary_signatures_match_the_contract(name):
+    assert ", ".join(_prototypes()[name]) == CONTRACT[name]
+
+
+def test_binding_argtypes_match_the_header():
+    """Every ctypes declaration has the header's parameter count and kinds."""
+    lib = attn.load_library()
+    protos = _prototypes()
+    assert set(protos) == set(attn.EXPORTS)
+    for name, params in protos.items():
+        argtypes = getattr(lib, name).argtypes
+        assert len(argtypes) == len(params), name
+        for c_param, ct in zip(params, argtypes):
+            if "*" in c_param:
+                assert ct is ctypes.c_void_p, (name, c_param)
+            elif c_param.startswith("float"):
+                assert ct is ctypes.c_float, (name, c_param)
+            else:
+                assert ct is ctypes.c_int, (name, c_param)
+
+
 def test_library_exports_every_declared_symbol():
     lib = attn.load_library()
     for name in _declared_functions():
@@ -52,11 +97,14 @@ def _fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4, Hkv=2, Nq=256, Nk=
 
 
 def _varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cq=FAKE, ck=FAKE, S=3, Hq=4, Hkv=4,
-            mq=100, mk=100, d=64, scale=0.125, causal=0):
+            mq=100, mk=100, d=64, scale=0.125, causal=0, order=None, ordered=False):
     lib = attn.load_library()
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.attn_fwd_varlen(vp(q), vp(k), vp(v), vp(o), vp(lse), vp(cq), vp(ck), S, Hq, Hkv,
-                               mq, mk, d, scale, causal, None, None)
+    args = (vp(q), vp(k), vp(v), vp(o), vp(lse), vp(cq), vp(ck), S, Hq, Hkv, mq, mk, d, scale,
+            causal)
+    if ordered:
+        return lib.attn_fwd_varlen_ordered(*args, vp(order), None)
+    return lib.attn_fwd_varlen(*args, None)
 
 
 def _plan(cq=FAKE, ck=FAKE, S=3, mq=100, mk=100, causal=1, order=FAKE):
@@ -98,8 +146,11 @@ def test_attn_varlen_plan_empty_is_a_noop():
     (dict(Nk=-1), attn.ATTN_ERR_SIZE),
     (dict(scale=float("nan")), attn.ATTN_ERR_SIZE),
     (dict(scale=float("inf")), attn.ATTN_ERR_SIZE),
-    (dict(scale=0.0), attn.ATTN_ERR_SIZE),
-    (dict(scale=-0.1), attn.ATTN_ERR_SIZE),
+    (dict(scale=float("-inf")), attn.ATTN_ERR_SIZE),
+    # any finite scale passes validation (the null pointer stops the call next)
+    (dict(scale=0.0, q=None), attn.ATTN_ERR_NULL),
+    (dict(scale=-0.1, q=None), attn.ATTN_ERR_NULL),
+    (dict(scale=-1e30, lse=None), attn.ATTN_ERR_NULL),
     (dict(q=FAKE + 8), attn.ATTN_ERR_ALIGN),
     (dict(o=FAKE + 2), attn.ATTN_ERR_ALIGN),
     (dict(k=FAKE + 4), attn.ATTN_ERR_ALIGN),
@@ -136,11 +187,21 @@ def test_attn_fwd_keys_may_be_null_when_there_are_no_keys():
 ])
 def test_attn_fwd_varlen_rejects_bad_arguments(kw, code):
     assert _varlen(**kw) == code
+    # the ordered variant validates the same way (a NULL order means index order)
+    assert _varlen(ordered=True, **kw) == code
+    assert _varlen(ordered=True, order=FAKE, **kw) == code
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, -3.0])
+def test_attn_fwd_varlen_accepts_every_finite_scale(scale):
+    assert _varlen(scale=scale, q=None) == attn.ATTN_ERR_NULL
+    assert _varlen(scale=scale, q=None, ordered=True, order=FAKE) == attn.ATTN_ERR_NULL
 
 
 def test_attn_fwd_varlen_empty_is_a_noop():
     assert _varlen(q=None, cq=None, ck=None, S=0) == attn.ATTN_OK
     assert _varlen(q=None, cq=None, ck=None, mq=0) == attn.ATTN_OK
+    assert _varlen(q=None, cq=None, ck=None, S=0, ordered=True) == attn.ATTN_OK
 
 
 def test_binding_refuses_cpu_tensors():
@@ -183,7 +244,8 @@ def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv
     (dict(B=-1), attn.ATTN_ERR_SIZE),
     (dict(Nq=-1), attn.ATTN_ERR_SIZE),
     (dict(scale=float("nan")), attn.ATTN_ERR_SIZE),
-    (dict(scale=0.0), attn.ATTN_ERR_SIZE),
+    (dict(scale=0.0, ws=None), attn.ATTN_ERR_NULL),     # finite scales pass validation
+    (dict(scale=-0.25, dq=None), attn.ATTN_ERR_NULL),
     (dict(ws=FAKE + 8), attn.ATTN_ERR_ALIGN),
     (dict(dq=FAKE + 2), attn.ATTN_ERR_ALIGN),
     (dict(dv=FAKE + 4), attn.ATTN_ERR_ALIGN),
@@ -202,12 +264,14 @@ def test_attn_bwd_empty_problem_is_a_noop():
 
 def _bwd_varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
                 ws=FAKE, cq=FAKE, ck=FAKE, S=3, Tq=600, Hq=4, Hkv=2, mq=256, mk=256, d=128,
-                scale=0.088, causal=1, order=None):
+                scale=0.088, causal=1, order=None, ordered=False):
     lib = attn.load_library()
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.attn_bwd_varlen(vp(q), vp(k), vp(v), vp(o), vp(lse), vp(do), vp(dq), vp(dk), vp(dv),
-                               vp(ws), vp(cq), vp(ck), S, Tq, Hq, Hkv, mq, mk, d, scale, causal,
-                               vp(order), None)
+    args = (vp(q), vp(k), vp(v), vp(o), vp(lse), vp(do), vp(dq), vp(dk), vp(dv), vp(ws), vp(cq),
+            vp(ck), S, Tq, Hq, Hkv, mq, mk, d, scale, causal)
+    if ordered:
+        return lib.attn_bwd_varlen_ordered(*args, vp(order), None)
+    return lib.attn_bwd_varlen(*args, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -229,6 +293,8 @@ def _bwd_varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=F
 ])
 def test_attn_bwd_varlen_rejects_bad_arguments(kw, code):
     assert _bwd_varlen(**kw) == code
+    assert _bwd_varlen(ordered=True, **kw) == code
+    assert _bwd_varlen(ordered=True, order=FAKE, **kw) == code
 
 
 def test_attn_bwd_varlen_empty_problem_is_a_noop():
@@ -265,7 +331,8 @@ def _dims(d_qk, d_v, **kw):
     (192, 128, dict(o=FAKE + 2), attn.ATTN_ERR_ALIGN),
     (192, 128, dict(Hq=3, Hkv=2), attn.ATTN_ERR_HEADS),
     (192, 128, dict(Nk=-1), attn.ATTN_ERR_SIZE),
-    (192, 128, dict(scale=-1.0), attn.ATTN_ERR_SIZE),
+    (192, 128, dict(scale=float("nan")), attn.ATTN_ERR_SIZE),
+    (192, 128, dict(scale=-1.0, q=None), attn.ATTN_ERR_NULL),
 ])
 def test_attn_fwd_dims_rejects_bad_arguments(d_qk, d_v, kw, code):
     assert _dims(d_qk, d_v, **kw) == code
@@ -324,3 +391,15 @@ def _probe(ops=FAKE, shape=32, iters=16, wg=2, sink=FAKE, clocks=FAKE):
 ])
 def test_attn_probe_mfma_rejects_bad_arguments(kw, code):
     assert _probe(**kw) == code
+
+
+@pytest.mark.parametrize("wg,ids,code", [
+    (4, None, attn.ATTN_ERR_NULL),
+    (0, FAKE, attn.ATTN_ERR_SIZE),
+    (-1, FAKE, attn.ATTN_ERR_SIZE),
+    (4, FAKE + 4, attn.ATTN_ERR_ALIGN),
+    (1 << 30, FAKE, attn.ATTN_ERR_TOO_LARGE),
+])
+def test_attn_probe_xcd_rejects_bad_arguments(wg, ids, code):
+    lib = attn.load_library()
+    assert lib.attn_probe_xcd(wg, None if ids is None else ctypes.c_void_p(ids), None) == code

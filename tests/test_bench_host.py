@@ -28,13 +28,27 @@ def test_string_literals_are_code():
     assert bench._code_tokens(a) != bench._code_tokens('const char* s = "a";')
 
 
-def test_committed_summaries_match_the_current_code():
-    """The forward summaries in profiles/ were taken on the code as it stands."""
+def test_traffic_is_reported_only_for_the_current_code(tmp_path):
+    """A summary's traffic figure is used only while the forward's code is the one it was taken on."""
+    sha = bench.kernel_source_sha256()
+    (tmp_path / "attn_fwd_w1.md").write_text(
+        f"# x\n\ntraffic_bytes_per_launch: 12345\nkernel_source_sha256: {sha}\n")
+    (tmp_path / "attn_fwd_w2.md").write_text(
+        "# x\n\ntraffic_bytes_per_launch: 12345\nkernel_source_sha256: " + "0" * 64 + "\n")
+    assert bench.measured_traffic("w1", str(tmp_path)) == 12345.0
+    assert bench.measured_traffic("w2", str(tmp_path)) is None
+    assert bench.measured_traffic("w3", str(tmp_path)) is None
+
+
+def test_committed_summaries_record_their_code_and_traffic():
+    """Every forward summary in profiles/ names the code hash it was taken on and its traffic."""
     import glob
     import os
-    sha = bench.kernel_source_sha256()
+    import re
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     files = glob.glob(os.path.join(root, "profiles", "attn_fwd_*.md"))
     assert files
     for f in files:
-        assert f"kernel_source_sha256: {sha}" in open(f).read(), os.path.basename(f)
+        text = open(f).read()
+        assert re.search(r"^kernel_source_sha256: [0-9a-f]{64}$", text, re.M), os.path.basename(f)
+        assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M), os.path.basename(f)

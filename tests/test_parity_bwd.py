@@ -36,6 +36,11 @@ SMALL = [
     (3, 257, 257, 2, 2, False, True),
     (1, 1, 1, 1, 1, True, False),
     (1, 300, 45, 4, 1, True, False),
+    # dQ workgroups pack 8 query heads (G = 8, 16) and several groups per unit (G = 6, 16)
+    (1, 300, 300, 16, 2, True, True),
+    (2, 257, 257, 6, 1, True, False),
+    (1, 200, 333, 16, 1, False, False),
+    (1, 390, 390, 12, 1, True, True),
 ]
 
 
@@ -86,6 +91,60 @@ def test_backward_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded, d
 
 
 @pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("B,N,Hq,Hkv,causal,padded", [
+    (2, 700, 8, 2, True, False),     # 4 heads per dQ workgroup
+    (1, 333, 16, 2, True, True),     # 8 heads per dQ workgroup, key padding
+    (2, 517, 6, 1, True, False),     # 2 heads per dQ workgroup, 3 workgroups per row block
+    (1, 300, 16, 1, False, False),   # 8 heads, 2 workgroups per row block, non-causal
+])
+def test_backward_grouped_heads_dq_equals_repeated_kv_heads_bitwise(B, N, Hq, Hkv, causal, padded,
+                                                                   d):
+    """dQ of a GQA call equals dQ of the MHA call with K and V repeated G times, bit for bit.
+
+    The dQ kernel packs up to 8 query heads of a KV group into a workgroup
+    (256 / heads rows each) while the MHA call takes one head per workgroup.
+    A row's arithmetic does not depend on that: keys past a row's causal
+    limit add exact zeros, and D and the LSE come from forwards that are
+    themselves bitwise equal.
+    """
+    G = Hq // Hkv
+    q, k, v = inputs.make_qkv(B, N, N, Hq, Hkv, d, 9050 + Hq + N + d, q_mult=3.0)
+    do = inputs.make_dout(q.shape, 9051 + N)
+    seqlens = inputs.make_seqlens(B, N // 2, N, 9052 + N) if padded else None
+    kr = k.repeat_interleave(G, dim=2).contiguous()
+    vr = v.repeat_interleave(G, dim=2).contiguous()
+    print(f"[parity-bwd] gqa dq bitwise B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal}",
+          flush=True)
+    dq1, _, _ = _fwd_bwd(q, k, v, do, 0.088, causal, seqlens)
+    dq2, _, _ = _fwd_bwd(q, kr, vr, do, 0.088, causal, seqlens)
+    assert torch.equal(dq1, dq2)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("scale_mult", [-1.0, 0.0])
+def test_backward_any_finite_scale_full_oracle(d, scale_mult):
+    """Negative and zero scales through the forward and the backward."""
+    B, N, Hq, Hkv = 2, 300, 4, 2
+    seed = 9070 + d + int(scale_mult)
+    q, k, v = inputs.make_qkv(B, N, N, Hq, Hkv, d, seed, q_mult=2.0)
+    do = inputs.make_dout(q.shape, seed + 1)
+    seqlens = inputs.make_seqlens(B, 1, N, seed + 2)
+    scale = scale_mult / math.sqrt(d)
+    for causal in (True, False):
+        print(f"[parity-bwd] scale={scale:.4f} d={d} causal={causal}", flush=True)
+        dq, dk, dv = _fwd_bwd(q, k, v, do, scale, causal, seqlens)
+        rq, rk, rv = oracle.attention_backward(to_np64(q), to_np64(k), to_np64(v), to_np64(do),
+                                               scale, causal, seqlens.numpy(), workers=8)
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            if scale == 0.0 and name != "dv":
+                # scores do not depend on Q or K: their gradients are exactly zero
+                assert (got == 0).all(), name
+                assert np.abs(ref).max() == 0.0, name
+                continue
+            assert_grad_parity(grad_errors(to_np64(got), ref), name)
+
+
+@pytest.mark.parametrize("d", [128, 64])
 def test_backward_is_deterministic(d):
     q, k, v = inputs.make_qkv(2, 700, 700, 8, 2, d, 9100, q_mult=3.0)
     do = inputs.make_dout(q.shape, 9101)
@@ -132,6 +191,8 @@ def _fwd_bwd_varlen(q, k, v, do, cq, ck, mq, mk, scale, causal, order=None):
 VARLEN = [
     # query lengths, key lengths (None: the same), Hq, Hkv, causal
     ([1, 130, 257, 0, 64, 200], None, 4, 2, True),
+    ([1, 130, 257, 0, 64, 200], None, 16, 2, True),
+    ([300, 7, 129], None, 6, 1, False),
     ([1, 130, 257, 0, 64, 200], None, 4, 4, False),
     ([64, 129, 5], [300, 17, 128], 2, 1, False),
     ([64, 129, 5, 0], [300, 17, 128, 40], 4, 1, True),

@@ -33,3 +33,22 @@ def test_probe_does_every_mfma_it_counts(value, shape):
     assert (c > 0).all()
     ghz = c[:, 0] / c[:, 1] * 0.1
     assert ((ghz > 0.3) & (ghz < 3.0)).all(), (ghz.min().item(), ghz.max().item())
+
+
+def test_workgroups_are_dealt_round_robin_to_the_xcds():
+    """The forward's grid order assumes workgroup w runs on XCD w % (number of XCDs).
+
+    The probe records the XCD of every workgroup of a grid several times the
+    CU count.  In single-partition mode all 8 XCDs appear and the mapping is
+    w % 8; a device partitioned to one XCD shows only XCD ids of one value.
+    """
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 4 * cus + 5
+    ids = attn.attn_probe_xcd(n).cpu()
+    xcc = ids[:, 0]
+    seen = sorted(set(xcc.tolist()))
+    print(f"[probe] {n} workgroups, XCDs seen {seen}, CUs {cus}", flush=True)
+    assert ((xcc >= 0) & (xcc < 8)).all()
+    if len(seen) > 1:
+        assert len(seen) == 8
+        assert torch.equal(xcc, torch.arange(n, dtype=torch.int32) % 8)

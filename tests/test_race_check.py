@@ -1,0 +1,87 @@
+"""GPU race check: the conservatively synchronised build gives the tuned build's outputs bit for bit.
+
+libattn_safe.so is compiled from the same sources with ATTN_FORCE_SAFE=1: the
+two wave groups of the ping-pong kernel run in lockstep instead of half a
+period apart, every LDS store and global load is waited for and followed by a
+workgroup barrier, and the d = 64 kernel waits for its tile DMA before it
+computes.  The arithmetic and its order are unchanged, so any difference from
+the tuned build points at a missing wait or barrier there.  The cases cover
+the headline workload at full size (paired work items, four query heads per
+workgroup), a small paired grid, the unpaired d = 64 kernel with key padding,
+the packed form with its LPT order, the block-sparse tile list and the
+(192, 128) head dimensions.
+"""
+
+import os
+
+import pytest
+import torch
+
+from exact_attention_18_amd import attn, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _both(fn):
+    """fn() under the tuned library, then under the race-check build."""
+    if not os.path.exists(attn.SAFE_LIB_PATH):
+        pytest.fail("libattn_safe.so is not built (build() compiles it)")
+    a = fn()
+    torch.cuda.synchronize()
+    with attn.using_library(attn.SAFE_LIB_PATH):
+        b = fn()
+        torch.cuda.synchronize()
+    return a, b
+
+
+def _assert_same(a, b):
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,d,causal,padded", [
+    (2, 1000, 8, 2, 128, True, False),   # paired items, 4 heads per workgroup
+    (2, 517, 4, 4, 128, False, True),    # paired, one head per workgroup, key padding
+    (4, 700, 4, 4, 64, False, True),     # d = 64 kernel (direct-to-LDS tile loads)
+    (2, 600, 8, 8, 64, True, False),
+])
+def test_safe_build_matches_tuned_small(B, N, Hq, Hkv, d, causal, padded):
+    q, k, v = inputs.make_qkv(B, N, N, Hq, Hkv, d, 9600 + N + d, q_mult=3.0)
+    sl = inputs.make_seqlens(B, N // 3, N, 9601).to(DEV) if padded else None
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    print(f"[race] B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal}", flush=True)
+    _assert_same(*_both(lambda: attn.attn_fwd(qd, kd, vd, 0.09, causal, sl)))
+
+
+def test_safe_build_matches_tuned_other_entry_points():
+    lengths = torch.tensor([700, 1, 257, 0, 1500, 64], dtype=torch.int32)
+    cu = inputs.cu_from_lengths(lengths).to(DEV)
+    T, mx = int(lengths.sum()), int(lengths.max())
+    q, k, v = inputs.make_packed_qkv(T, T, 8, 2, 128, 9610, q_mult=3.0)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    plan = attn.attn_varlen_plan(cu, cu, mx, mx, True)
+    print("[race] varlen", flush=True)
+    _assert_same(*_both(lambda: attn.attn_fwd_varlen(qd, kd, vd, cu, cu, mx, mx, 0.09, True,
+                                                     seq_order=plan)))
+
+    q, k, v = inputs.make_qkv(2, 1000, 1000, 8, 2, 128, 9611, q_mult=3.0)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    g = torch.Generator().manual_seed(9612)
+    bm = (torch.rand((8, 8, 8), generator=g) < 0.4).to(torch.uint8).to(DEV)
+    print("[race] block-sparse", flush=True)
+    _assert_same(*_both(lambda: attn.attn_fwd_blocksparse(qd, kd, vd, bm, 0.09, True)))
+
+    q, k, v = inputs.make_qkv(2, 1000, 1000, 4, 4, 192, 9613, q_mult=2.0, d_v=128)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    print("[race] (192, 128)", flush=True)
+    _assert_same(*_both(lambda: attn.attn_fwd(qd, kd, vd, 0.07, True)))
+
+
+def test_safe_build_matches_tuned_headline_full_size():
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    x = inputs.workload_inputs(w)
+    qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    print(f"[race] {w.name}", flush=True)
+    _assert_same(*_both(lambda: attn.attn_fwd(qd, kd, vd, w.scale, w.causal)))
