@@ -34,9 +34,11 @@ ATTN_ERR_SIZE = -4
 ATTN_ERR_LAUNCH = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_TOO_LARGE = -7
+ATTN_ERR_SCRATCH = -8
 
 EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen",
-           "attn_fwd_varlen_ordered", "attn_varlen_plan", "attn_bwd", "attn_bwd_varlen",
+           "attn_fwd_varlen_ordered", "attn_varlen_plan", "attn_bwd", "attn_bwd_noalloc",
+           "attn_bwd_varlen",
            "attn_bwd_varlen_ordered", "attn_bwd_workspace_size",
            "attn_probe_mfma", "attn_probe_xcd", "attn_strerror", "attn_last_hip_error",
            "attn_version")
@@ -73,6 +75,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                              f32, i32, vp, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, f32, i32, vp, vp]
+    lib.attn_bwd_noalloc.restype = i32
     lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                     i32, i32, i32, i32, f32, i32, vp]
     lib.attn_bwd_varlen.restype = i32

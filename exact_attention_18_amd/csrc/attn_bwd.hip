@@ -49,6 +49,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "attn.h"
 #include "cdna4.h"
@@ -900,6 +901,47 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
                          causal != 0, st);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the LSE * log2(e) and D rows live in a static
+// device array instead of a caller workspace.  Each device holds its own copy
+// of the array; host code reaches it only through the address
+// hipGetSymbolAddress returns with that device current (the array's name is a
+// host-side stand-in, not a device address), kept per device.  Calls on one
+// device share the array, so calls that overlap on a device race; every
+// entry a call reads is written by that call's preprocess kernel first, so
+// nothing needs clearing between calls.
+constexpr size_t kScratchBytes = size_t(32) << 20;                   // 32 MiB per device
+constexpr long kScratchRows = long(kScratchBytes / (2 * sizeof(float)));  // (batch, head, row) triples
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (looked up once per device).
+int scratch_of_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    attn_detail::last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_TOO_LARGE;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      attn_detail::last_hip_error = static_cast<int>(e);
+      return ATTN_ERR_LAUNCH;
+    }
+    scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<float*>(scratch_ptr[dev]);
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -914,6 +956,22 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, Nq,
                  Nk, d, scale, causal, seqlens_k, stream);
 }
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                                int causal, const int32_t* seqlens_k, void* stream) {
+  bool noop = false;
+  const int rc = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, &noop);
+  if (rc != ATTN_OK || noop) return rc;
+  if ((long)B * Hq * Nq > kScratchRows) return ATTN_ERR_SCRATCH;
+  float* ws = nullptr;
+  const int src = scratch_of_current_device(&ws);
+  if (src != ATTN_OK) return src;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 seqlens_k, stream);
+}
+
 
 extern "C" int attn_bwd_varlen_ordered(const void* q, const void* k, const void* v,
                                        const void* o, const float* lse, const void* dout, void* dq,

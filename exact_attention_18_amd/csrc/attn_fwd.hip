@@ -1355,6 +1355,8 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed (see attn_last_hip_error)";
     case ATTN_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_TOO_LARGE: return "problem too large for 32-bit grid or row indexing";
+    case ATTN_ERR_SCRATCH:
+      return "B * Hq * Nq exceeds the 4194304 rows of attn_bwd_noalloc's static scratch";
     default: return "unknown attn status";
   }
 }

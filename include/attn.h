@@ -71,7 +71,8 @@ enum attn_status {
   ATTN_ERR_SIZE = -4,      /* negative size, or scale not finite                  */
   ATTN_ERR_LAUNCH = -5,    /* the HIP launch failed (see attn_last_hip_error)     */
   ATTN_ERR_ALIGN = -6,     /* q, k, v or o not 16-byte aligned, lse not 4-byte    */
-  ATTN_ERR_TOO_LARGE = -7  /* grid or index range exceeds what the kernel handles */
+  ATTN_ERR_TOO_LARGE = -7, /* grid or index range exceeds what the kernel handles */
+  ATTN_ERR_SCRATCH = -8    /* attn_bwd_noalloc: more rows than its static scratch  */
 };
 
 /*
@@ -268,6 +269,27 @@ int attn_bwd_varlen_ordered(const void* q, const void* k, const void* v, const v
                             const int32_t* cu_seqlens_k, int num_seqs, int total_q, int Hq,
                             int Hkv, int max_seqlen_q, int max_seqlen_k, int d, float scale,
                             int causal, const int32_t* seq_order, void* stream);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The LSE * log2(e) and D rows that
+ * attn_bwd keeps in the caller's workspace live instead in a static device
+ * array of 32 MiB, of which each GPU the library runs on holds its own copy
+ * until the process ends.  This call allocates nothing (no hipMalloc, no
+ * allocating library routine); its first call on a device looks up the
+ * array's device address there (hipGetSymbolAddress).
+ *   Arguments, results and errors: as for attn_bwd (without workspace), plus
+ *   ATTN_ERR_SCRATCH when B * Hq * Nq > 4194304 (nothing is launched).
+ * Every call on one GPU shares that GPU's array: calls that overlap on a GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Each call writes every array entry it reads before reading it, so
+ * what an earlier call left there never reaches a result.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
+                     void* stream);
 
 /* Bytes of workspace attn_bwd needs: two fp32 per (batch, query head, query
  * row); 0 when any argument is <= 0. */

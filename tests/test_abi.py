@@ -82,7 +82,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     codes = [attn.ATTN_OK, attn.ATTN_ERR_NULL, attn.ATTN_ERR_HEAD_DIM, attn.ATTN_ERR_HEADS,
-             attn.ATTN_ERR_SIZE, attn.ATTN_ERR_LAUNCH, attn.ATTN_ERR_ALIGN, attn.ATTN_ERR_TOO_LARGE]
+             attn.ATTN_ERR_SIZE, attn.ATTN_ERR_LAUNCH, attn.ATTN_ERR_ALIGN, attn.ATTN_ERR_TOO_LARGE,
+             attn.ATTN_ERR_SCRATCH]
     texts = [attn.strerror(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert "unknown" in attn.strerror(12345)
@@ -253,6 +254,35 @@ def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv
 ])
 def test_attn_bwd_rejects_bad_arguments(kw, code):
     assert _bwd(**kw) == code
+
+
+def _bwd_noalloc(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                 B=2, Hq=4, Hkv=2, Nq=256, Nk=256, d=128, scale=0.088, causal=1, seqlens=None):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_bwd_noalloc(vp(q), vp(k), vp(v), vp(o), vp(lse), vp(do), vp(dq), vp(dk),
+                                vp(dv), B, Hq, Hkv, Nq, Nk, d, scale, causal, vp(seqlens), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(dv=None), attn.ATTN_ERR_NULL),
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_HEADS),
+    (dict(B=-1), attn.ATTN_ERR_SIZE),
+    (dict(scale=float("nan")), attn.ATTN_ERR_SIZE),
+    (dict(dq=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    # rows beyond the static scratch are refused before any HIP call
+    (dict(B=1, Hq=32, Hkv=8, Nq=131073), attn.ATTN_ERR_SCRATCH),
+    (dict(B=65, Hq=16, Hkv=16, Nq=4096), attn.ATTN_ERR_SCRATCH),
+])
+def test_attn_bwd_noalloc_rejects_bad_arguments(kw, code):
+    assert _bwd_noalloc(**kw) == code
+
+
+def test_attn_bwd_noalloc_empty_problem_is_a_noop():
+    assert _bwd_noalloc(B=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None,
+                        dv=None) == attn.ATTN_OK
 
 
 def test_attn_bwd_empty_problem_is_a_noop():
