@@ -222,6 +222,41 @@ def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
     return out
 
 
+def softmax_issue(dev, budget_us: int = 20000, seed: int = 7):
+    """Issue cost of the softmax's exponential beside the matrix core (attn_probe_softmax_issue).
+
+    For each (MFMA wave on/off, exponential kind) the probe runs a full grid,
+    one 8-wave workgroup per CU, for budget_us of real time.  Reported per
+    case, as means over the waves of all CUs: shader cycles per MFMA of the
+    MFMA waves, shader cycles per softmax element of the softmax waves (one
+    element = one score's FMA, exp2, running-sum add, half a v_max3 and half
+    a bf16 pack, as in the forward), and the shader clock.
+    """
+    wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator().manual_seed(seed)
+    ops = (torch.rand((8, 64, 8), generator=g) * 2 - 1).to(torch.bfloat16).to(dev)
+    kinds = {0: "none", 1: "v_exp_f32", 2: "polynomial", 3: "polynomial_on_8_of_32"}
+    out = {"budget_us": budget_us, "workgroups": wg}
+    for mfma_on in (1, 0):
+        for kind in (0, 1, 2, 3):
+            if not mfma_on and kind == 0:
+                continue
+            _, st = attn.attn_probe_softmax_issue(ops, bool(mfma_on), kind, budget_us, wg)
+            torch.cuda.synchronize()
+            st = st.cpu().to(torch.float64).view(wg, 8, 4)
+            case = {}
+            if mfma_on:
+                m = st[:, :4]
+                case["mfma_cycles_per_mfma"] = round(float((m[..., 1] / (m[..., 0] * 16)).mean()), 2)
+                case["clock_ghz"] = round(float((m[..., 1] / m[..., 2]).mean()) * 0.1, 3)
+            if kind:
+                v = st[:, 4:]
+                case["softmax_cycles_per_element"] = round(float((v[..., 1] / (v[..., 0] * 32)).mean()), 3)
+                case.setdefault("clock_ghz", round(float((v[..., 1] / v[..., 2]).mean()) * 0.1, 3))
+            out[("mfma+" if mfma_on else "") + kinds[kind]] = case
+    return out
+
+
 def warm_up(step, n):
     """Runs n untimed warm-up steps; returns the first one's time in ms (cold caches), or None."""
     if n <= 0:
@@ -313,6 +348,12 @@ def main():
                     help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the sustained matrix-core rate measurement (attn_probe_mfma)")
+    ap.add_argument("--library", default=None, metavar="PATH",
+                    help="time another build of the library (e.g. "
+                         "exact_attention_18_amd/libattn_exp2poly.so) instead of libattn.so")
+    ap.add_argument("--softmax-issue", action="store_true",
+                    help="only measure the issue cost of the softmax's exp2 (hardware or polynomial) "
+                         "beside a wave streaming MFMAs (attn_probe_softmax_issue), one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device-to-device copies of BYTES bytes (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of the forward to bytes)")
@@ -327,6 +368,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.softmax_issue:
+        print(json.dumps({"softmax_issue": softmax_issue(dev)}), flush=True)
+        return
     if args.copy_calibration:
         n = args.copy_calibration // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -336,6 +380,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "copies": args.steps}), flush=True)
         return
+    if args.library:
+        lib_ctx = attn.using_library(os.path.abspath(args.library))
+        lib_ctx.__enter__()
     w = inputs.WORKLOADS[args.workload]
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     x = inputs.workload_inputs(w)
@@ -381,6 +428,8 @@ def main():
     cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "d_v": w.d_v,
            "causal": w.causal, "q_mult": w.q_mult, "algorithmic_flop": flops,
            "parallelism": "single GPU"}
+    if args.library:
+        cfg["library"] = os.path.basename(args.library)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -400,7 +449,8 @@ def main():
         "pct_of_mfma_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5)},
+                     "traffic": None if args.library else measured_traffic(w.name),
+                     "kernel_ms": round(kernel_ms, 5)},
         "mfma_sustained": probe,
         "cpu_baseline": cpu,
     }

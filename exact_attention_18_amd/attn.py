@@ -24,6 +24,9 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 # (compiled with ATTN_FORCE_SAFE=1); used only to check that the tuned build
 # has no missing wait or barrier.
 SAFE_LIB_PATH = os.path.join(_PKG, "libattn_safe.so")
+# The software-exp2 build: 8 of every 32 exponentials of the d = 128 softmax
+# as a polynomial on the FMA pipe (compiled with ATTN_EXP2_POLY=8).
+EXP2POLY_LIB_PATH = os.path.join(_PKG, "libattn_exp2poly.so")
 
 # attn_status codes (include/attn.h)
 ATTN_OK = 0
@@ -40,7 +43,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_dims", "attn_fwd_blocksparse", "attn_fwd_varlen
            "attn_fwd_varlen_ordered", "attn_varlen_plan", "attn_bwd", "attn_bwd_noalloc",
            "attn_bwd_varlen",
            "attn_bwd_varlen_ordered", "attn_bwd_workspace_size",
-           "attn_probe_mfma", "attn_probe_xcd", "attn_strerror", "attn_last_hip_error",
+           "attn_probe_mfma", "attn_probe_softmax_issue", "attn_probe_xcd", "attn_strerror",
+           "attn_last_hip_error",
            "attn_version")
 
 _lib = None
@@ -88,6 +92,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_probe_mfma.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.attn_probe_mfma.restype = i32
+    lib.attn_probe_softmax_issue.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.attn_probe_softmax_issue.restype = i32
     lib.attn_probe_xcd.argtypes = [i32, vp, vp]
     lib.attn_probe_xcd.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -487,3 +493,24 @@ def attn_probe_xcd(workgroups: int, device=None) -> torch.Tensor:
     rc = load_library().attn_probe_xcd(int(workgroups), _ptr(ids), _stream_handle(dev))
     _check(rc, "attn_probe_xcd")
     return ids
+
+
+def attn_probe_softmax_issue(operands: torch.Tensor, mfma_on: bool, exp_kind: int, budget_us: int,
+                             workgroups: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Launch the softmax issue probe; returns (values fp32 [64, 32], stats int64 [wg * 8, 4]).
+
+    exp_kind: 0 none, 1 v_exp_f32, 2 polynomial exp2, 3 polynomial on 8 of 32
+    elements.  stats[w] = (iterations, shader ticks, 100 MHz ticks, checksum
+    bits) of wave w (attn_probe_softmax_issue in include/attn.h).
+    """
+    _need(operands, "operands", torch.bfloat16)
+    if tuple(operands.shape) != (8, 64, 8):
+        raise ValueError(f"operands must be [8, 64, 8], got {tuple(operands.shape)}")
+    dev = operands.device
+    values = torch.zeros((64, 32), dtype=torch.float32, device=dev)
+    stats = torch.empty((workgroups * PROBE_WAVES, 4), dtype=torch.int64, device=dev)
+    rc = load_library().attn_probe_softmax_issue(_ptr(operands), int(bool(mfma_on)), int(exp_kind),
+                                                 int(budget_us), int(workgroups), _ptr(values),
+                                                 _ptr(stats), _stream_handle(dev))
+    _check(rc, "attn_probe_softmax_issue")
+    return values, stats

@@ -25,6 +25,9 @@ LIB = os.path.join(PKG, "libattn.so")
 # The race-check variant: the same kernels with conservative synchronisation
 # (ATTN_FORCE_SAFE); its outputs must equal libattn.so's bit for bit.
 SAFE_LIB = os.path.join(PKG, "libattn_safe.so")
+# The software-exp2 variant: 8 of every 32 exponentials of the d = 128 softmax
+# on the FMA pipe (ATTN_EXP2_POLY=8); measured slower, so not the default.
+EXP2POLY_LIB = os.path.join(PKG, "libattn_exp2poly.so")
 ARCH = "gfx950"
 
 
@@ -75,14 +78,16 @@ def _finish(out: str, proc: subprocess.Popen, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False, extra=(), safe: bool = True) -> str:
-    """Compile libattn.so (and, with safe, the race-check libattn_safe.so); returns libattn.so's path.
+def build(verbose: bool = False, extra=(), variants: bool = True) -> str:
+    """Compile libattn.so (and, with variants, libattn_safe.so and libattn_exp2poly.so).
 
-    The two compiles run side by side.  Raises on compiler failure.
+    The compiles run side by side.  Returns libattn.so's path; raises on
+    compiler failure.
     """
     jobs = [(LIB, _compile(LIB, extra, verbose))]
-    if safe:
+    if variants:
         jobs.append((SAFE_LIB, _compile(SAFE_LIB, (*extra, "-DATTN_FORCE_SAFE=1"), verbose)))
+        jobs.append((EXP2POLY_LIB, _compile(EXP2POLY_LIB, (*extra, "-DATTN_EXP2_POLY=8"), verbose)))
     for out, proc in jobs:
         _finish(out, proc, verbose)
     return LIB

@@ -107,6 +107,7 @@ struct Tile {
 };
 
 constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
+constexpr float kTwoPowTau = 256.0f;  // 2^kTau
 
 // Race check.  A library built with -DATTN_FORCE_SAFE=1 keeps every
 // arithmetic step and its order but synchronises conservatively: the two
@@ -120,6 +121,15 @@ constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
 #define ATTN_FORCE_SAFE 0
 #endif
 constexpr bool kForceSafe = ATTN_FORCE_SAFE != 0;
+
+// Exponentials of the d = 128 softmax evaluated on the FMA pipe (exp2_poly)
+// instead of v_exp_f32: this many of the 32 per lane and key tile (0, 4, 8
+// or 16; element e of a lane's tile when e % 8 < count / 4).
+#ifndef ATTN_EXP2_POLY
+#define ATTN_EXP2_POLY 0
+#endif
+constexpr int kExp2Poly = ATTN_EXP2_POLY;
+static_assert(kExp2Poly == 0 || kExp2Poly == 4 || kExp2Poly == 8 || kExp2Poly == 16, "exp2 split");
 
 struct Params {
   const __bf16* q;
@@ -842,43 +852,70 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         }
     };
     // ---- VALU phase: online softmax of S_j -> P_j, O rescale when the max moved.
-    auto vphase = [&](int j) __attribute__((always_inline)) {
-      const int tile = tile_of(j);
-      if (needs_mask(tile)) apply_mask(tile);
-      float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 32; e += 4) {
-        m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
-        m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
-      }
-      const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
-      // The rescale (new max, alpha, l and O scaled) runs only when some row's
-      // max grew by more than tau; the test is wave-uniform, and otherwise
-      // alpha would be exactly 1.
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
-      }
-      float ls0 = 0.f, ls1 = 0.f;
+    // Exponentials of the tile against the running max, packed to bf16 into
+    // pv_op; returns this lane's partial row sum in ls0 + ls1.
+    auto exps = [&](float& ls0, float& ls1) __attribute__((always_inline)) {
+      auto expo = [](int e, float x) __attribute__((always_inline)) {
+        return (e % 8) < kExp2Poly / 4 ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
+      };
 #pragma unroll
       for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], c, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kt][r + 1], c, -m_use));
-          ls0 += e0;
-          ls1 += e1;
+          const float e0 = expo(16 * kt + r, fmaf(sv[kt][r], c, -m_use));
+          const float e1 = expo(16 * kt + r + 1, fmaf(sv[kt][r + 1], c, -m_use));
+          if (kt == 0 && r == 0) {
+            ls0 = e0;
+            ls1 = e1;
+          } else {
+            ls0 += e0;
+            ls1 += e1;
+          }
           const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
           uint32_t u = __builtin_bit_cast(uint32_t, pk);
           asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
           pv_op[kt][r >> 3][(r & 7) >> 1] = u;
         }
       asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
+    };
+    auto vphase = [&](int j) __attribute__((always_inline)) {
+      const int tile = tile_of(j);
+      if (needs_mask(tile)) apply_mask(tile);
+      float ls0, ls1;
+      // Once every row of the wave has a running max, the exponentials are
+      // taken against it first.  A lane's partial sum bounds each of its
+      // exponentials, so when no lane's sum exceeds 2^tau no score of the
+      // tile exceeds its row's max by more than tau: the rescale would not
+      // fire and the tile is done without its row maxima.  Otherwise the
+      // exact step below runs (and decides as before), so the results are
+      // bitwise those of that step alone.
+      bool done = false;
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+        exps(ls0, ls1);
+        done = __builtin_amdgcn_ballot_w64(ls0 + ls1 > kTwoPowTau) == 0;
+      }
+      if (!done) {
+        float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 32; e += 4) {
+          m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
+          m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
+        }
+        const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
+        // The rescale (new max, alpha, l and O scaled) runs only when some
+        // row's max grew by more than tau; the test is wave-uniform, and
+        // otherwise alpha would be exactly 1.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          m_use = (m_new == -INFINITY) ? 0.f : m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
+        }
+        exps(ls0, ls1);
+      }
       l_run += ls0 + ls1;
     };
 

@@ -70,6 +70,26 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// exp2 on the FMA pipe (FlashAttention-4 (papercache summary), section
+// 3.1.3, the exponential emulated by a polynomial): Cody-Waite split
+// x = n + f, n = floor(x), f in [0, 1); 2^f by a degree-3 polynomial with
+// p(0) = 1 whose coefficients are the relative-error minimax fit on [0, 1]
+// (Remez exchange; max relative error 8.6e-5 in fp32, far below the 2^-9
+// of the bf16 rounding that follows); 2^n inserted by adding n to the
+// exponent bits.  x is clamped at -127: there n = -127 and f = 0 give exactly
+// +0, so a masked score (-inf) still contributes nothing.  Valid for x < 128.
+constexpr float kExp2C1 = 0x1.63e658p-1f;
+constexpr float kExp2C2 = 0x1.d2378ap-3f;
+constexpr float kExp2C3 = 0x1.3baaa6p-4f;
+
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = __builtin_fmaxf(x, -127.f);
+  const float n = __builtin_floorf(x);
+  const float f = x - n;
+  const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, 1.f);
+  return __int_as_float(__float_as_int(p) + (static_cast<int>(n) << 23));
+}
+
 // Two transpose reads of LDS, concatenated into one 8-element bf16 operand.
 __device__ __forceinline__ bf16x8 read_tr_pair(const __bf16* p0, const __bf16* p1) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;

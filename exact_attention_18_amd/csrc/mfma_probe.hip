@@ -126,7 +126,150 @@ __global__ __launch_bounds__(kProbeThreads, 1) void xcd_probe_kernel(int32_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Softmax issue probe: what the exponential costs beside the matrix core.
+//
+// FlashAttention-4 (papercache summary), section 3.1.3, evaluates part of
+// each row's exp2 as a polynomial on the FMA units because on its hardware
+// the exponential unit, not the FMA pipes, limits the softmax.  On CDNA4 the
+// exponential issues from the same VALU as an FMA, so the question is what
+// each form costs in VALU issue, with the other wave of the SIMD streaming
+// MFMAs as in the forward's ping-pong.  Waves 0-3 stream the forward's MFMA
+// (or idle); waves 4-7, one per SIMD beside them, run a softmax-shaped loop:
+// per lane and iteration 32 elements, each x = s * c - m (one FMA), e = exp2(x),
+// a running sum, a running max (v_max3 over pairs) and packing pairs to bf16 --
+// the forward's instruction mix.  The exponential is v_exp_f32 (kind 1), the
+// polynomial exp2_poly (kind 2), or the polynomial on 8 of the 32 elements
+// (kind 3, the share FlashAttention-4 emulates).  Every wave runs until a
+// fixed real-time budget has passed (s_memrealtime always advances, so every
+// wave ends) and records its iterations and shader-clock ticks.
+
+// The polynomial is exp2_poly (cdna4.h), the one the forward can use.
+template <int KIND>
+__global__ __launch_bounds__(kProbeThreads, 1) void softmax_issue_probe_kernel(
+    const bf16x8* __restrict__ ops, int mfma_on, uint64_t budget, float c, float dm,
+    float* __restrict__ values, uint64_t* __restrict__ stats) {
+  __shared__ float reserve[kProbeLdsFloats];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint64_t iters = 0, t0 = 0, t1 = 0, r0 = 0, r1 = 0;
+  float chk = 0.f;
+  __syncthreads();
+  if (wave < 4) {
+    if (mfma_on) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = ops[i * 64 + lane];
+        b[i] = ops[(4 + i) * 64 + lane];
+      }
+      f32x16 acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+      r0 = __builtin_amdgcn_s_memrealtime();
+      t0 = __builtin_amdgcn_s_memtime();
+      do {
+        static_for<0, 16>([&](auto I) __attribute__((always_inline)) {
+          constexpr int k = decltype(I)::value;
+          acc[k % 8] = mfma32(a[k % 4], b[(k + k / 4) % 4], acc[k % 8]);
+        });
+        ++iters;
+      } while (__builtin_amdgcn_s_memrealtime() - r0 < budget);
+      t1 = __builtin_amdgcn_s_memtime();
+      r1 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) chk += acc[i][e];
+    }
+  } else if constexpr (KIND != 0) {
+    float sc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sc[i] = (lane + 64 * i) * (1.f / 256.f) - 8.f;  // x in [-8, 0)
+    // element i of the loop: polynomial (kind 2, or kind 3 on 8 of the 32), else v_exp_f32
+    auto ex = [](int i, float x) __attribute__((always_inline)) {
+      return (KIND == 2 || (KIND == 3 && i % 8 < 2)) ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
+    };
+    if (blockIdx.x == 0 && wave == 4) {  // the loop's first exponentials, for an accuracy check
+#pragma unroll
+      for (int i = 0; i < 32; ++i) values[lane * 32 + i] = ex(i, fmaf(sc[i], c, -0.f));
+    }
+    float m = 0.f, l0 = 0.f, l1 = 0.f, mx = -INFINITY;
+    uint32_t pk_x = 0;
+    r0 = __builtin_amdgcn_s_memrealtime();
+    t0 = __builtin_amdgcn_s_memtime();
+    do {
+#pragma unroll
+      for (int i = 0; i < 32; i += 2) {
+        const float e0 = ex(i, fmaf(sc[i], c, -m));
+        const float e1 = ex(i + 1, fmaf(sc[i + 1], c, -m));
+        l0 += e0;
+        l1 += e1;
+        mx = max3f(mx, e0, e1);
+        const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+        pk_x ^= __builtin_bit_cast(uint32_t, pk);
+      }
+      m += dm;
+      ++iters;
+    } while (__builtin_amdgcn_s_memrealtime() - r0 < budget);
+    t1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
+    chk = l0 + l1 + mx + static_cast<float>(pk_x & 0xffu);
+  }
+  volatile float* res = reserve;  // keeps the LDS reservation
+  res[threadIdx.x] = chk;
+  if (lane == 0) {
+    const long w = (long)blockIdx.x * kProbeWaves + wave;
+    stats[4 * w] = iters;
+    stats[4 * w + 1] = t1 - t0;
+    stats[4 * w + 2] = r1 - r0;
+    stats[4 * w + 3] = __float_as_uint(res[threadIdx.x]);
+  }
+}
+
 }  // namespace
+
+extern "C" int attn_probe_softmax_issue(const void* operands, int mfma_on, int exp_kind,
+                                        int budget_us, int workgroups, float* values,
+                                        uint64_t* stats, void* stream) {
+  if (operands == nullptr || values == nullptr || stats == nullptr) return ATTN_ERR_NULL;
+  if ((mfma_on != 0 && mfma_on != 1) || exp_kind < 0 || exp_kind > 3 || budget_us < 1 ||
+      budget_us > 10000000 || workgroups < 1)
+    return ATTN_ERR_SIZE;
+  if ((reinterpret_cast<uintptr_t>(operands) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(values) & 3u) != 0 || (reinterpret_cast<uintptr_t>(stats) & 7u) != 0)
+    return ATTN_ERR_ALIGN;
+  if (workgroups > (INT32_MAX / kProbeThreads)) return ATTN_ERR_TOO_LARGE;
+  (void)hipGetLastError();
+  const auto* ops = static_cast<const bf16x8*>(operands);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint64_t budget = static_cast<uint64_t>(budget_us) * 100u;  // s_memrealtime runs at 100 MHz
+  const float c = 1.f, dm = 1e-7f;
+  switch (exp_kind) {
+    case 0:
+      hipLaunchKernelGGL(softmax_issue_probe_kernel<0>, dim3(workgroups), dim3(kProbeThreads), 0, st,
+                         ops, mfma_on, budget, c, dm, values, stats);
+      break;
+    case 1:
+      hipLaunchKernelGGL(softmax_issue_probe_kernel<1>, dim3(workgroups), dim3(kProbeThreads), 0, st,
+                         ops, mfma_on, budget, c, dm, values, stats);
+      break;
+    case 2:
+      hipLaunchKernelGGL(softmax_issue_probe_kernel<2>, dim3(workgroups), dim3(kProbeThreads), 0, st,
+                         ops, mfma_on, budget, c, dm, values, stats);
+      break;
+    default:
+      hipLaunchKernelGGL(softmax_issue_probe_kernel<3>, dim3(workgroups), dim3(kProbeThreads), 0, st,
+                         ops, mfma_on, budget, c, dm, values, stats);
+      break;
+  }
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    attn_detail::last_hip_error = static_cast<int>(err);
+    return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
 
 extern "C" int attn_probe_xcd(int workgroups, int32_t* ids, void* stream) {
   if (ids == nullptr) return ATTN_ERR_NULL;

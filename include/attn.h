@@ -333,6 +333,35 @@ int attn_probe_mfma(const void* operands, int shape, int iters, int workgroups, 
                     uint64_t* clocks, void* stream);
 
 /*
+ * Softmax issue probe (a measurement aid; it computes nothing of the
+ * attention).  FlashAttention-4 (papercache summary), section 3.1.3,
+ * evaluates part of each row's exp2 as a polynomial on the FMA units because
+ * its exponential unit limits the softmax.  This call prices that choice on
+ * this device: in each 512-thread workgroup (one per CU, as the forward's),
+ * waves 0-3 stream the forward's MFMA (mfma_on = 1) or idle (0), and waves
+ * 4-7, one beside each of them on its SIMD, run the forward's softmax
+ * instruction mix on 32 elements per lane and iteration (FMA, exp2, running
+ * sum, v_max3, bf16 packing).  exp_kind: 0 = those waves idle,
+ * 1 = v_exp_f32, 2 = a degree-3 polynomial exp2 on the FMA pipe (Cody-Waite
+ * split, own minimax coefficients), 3 = the polynomial on 8 of the 32
+ * elements and v_exp_f32 on the rest.  Every wave runs until budget_us
+ * microseconds of real time have passed.
+ *   operands  : device bf16 [8][64][8], 16-byte aligned, as attn_probe_mfma.
+ *   values    : device fp32 [64 * 32], written when exp_kind != 0: lane l's
+ *               exponentials of x_i = (l + 64 i) / 256 - 8, i = 0..31, by
+ *               the kind's method (for an accuracy check).
+ *   stats     : device uint64 [workgroups * 8][4], written per wave:
+ *               iterations (16 MFMAs, or 32 elements per lane), shader-clock
+ *               ticks (s_memtime), 100 MHz ticks (s_memrealtime), and a
+ *               checksum's bits (keeps the work live).  Idle waves write 0.
+ *   budget_us : 1 .. 10000000.   workgroups : >= 1.
+ * Returns ATTN_ERR_NULL, ATTN_ERR_SIZE, ATTN_ERR_ALIGN, ATTN_ERR_TOO_LARGE
+ * or ATTN_ERR_LAUNCH; asynchronous on stream.
+ */
+int attn_probe_softmax_issue(const void* operands, int mfma_on, int exp_kind, int budget_us,
+                             int workgroups, float* values, uint64_t* stats, void* stream);
+
+/*
  * Workgroup placement probe (a measurement aid; it computes nothing of the
  * attention).  The grid order of the forward keeps the key/value tiles of a
  * (batch, KV head) unit in one XCD's L2 by dealing units round-robin to the

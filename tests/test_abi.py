@@ -433,3 +433,28 @@ def test_attn_probe_mfma_rejects_bad_arguments(kw, code):
 def test_attn_probe_xcd_rejects_bad_arguments(wg, ids, code):
     lib = attn.load_library()
     assert lib.attn_probe_xcd(wg, None if ids is None else ctypes.c_void_p(ids), None) == code
+
+
+def _issue(ops=FAKE, mfma_on=1, kind=1, budget=100, wg=2, values=FAKE, stats=FAKE):
+    lib = attn.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.attn_probe_softmax_issue(vp(ops), mfma_on, kind, budget, wg, vp(values), vp(stats),
+                                        None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ops=None), attn.ATTN_ERR_NULL),
+    (dict(values=None), attn.ATTN_ERR_NULL),
+    (dict(stats=None), attn.ATTN_ERR_NULL),
+    (dict(mfma_on=2), attn.ATTN_ERR_SIZE),
+    (dict(kind=4), attn.ATTN_ERR_SIZE),
+    (dict(kind=-1), attn.ATTN_ERR_SIZE),
+    (dict(budget=0), attn.ATTN_ERR_SIZE),
+    (dict(budget=10000001), attn.ATTN_ERR_SIZE),
+    (dict(wg=0), attn.ATTN_ERR_SIZE),
+    (dict(ops=FAKE + 8), attn.ATTN_ERR_ALIGN),
+    (dict(stats=FAKE + 4), attn.ATTN_ERR_ALIGN),
+    (dict(wg=1 << 30), attn.ATTN_ERR_TOO_LARGE),
+])
+def test_attn_probe_softmax_issue_rejects_bad_arguments(kw, code):
+    assert _issue(**kw) == code

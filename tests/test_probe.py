@@ -52,3 +52,26 @@ def test_workgroups_are_dealt_round_robin_to_the_xcds():
     if len(seen) > 1:
         assert len(seen) == 8
         assert torch.equal(xcc, torch.arange(n, dtype=torch.int32) % 8)
+
+
+@pytest.mark.parametrize("kind", [1, 2, 3])
+def test_softmax_issue_probe_computes_exp2_and_counts(kind):
+    """The probe's exponentials are exp2 (v_exp_f32, or the polynomial within its
+    8.6e-5 minimax bound plus fp32 rounding), and every wave reports work and ticks."""
+    import numpy as np
+    wg = torch.cuda.get_device_properties(0).multi_processor_count
+    ops = torch.full((8, 64, 8), 1.0, dtype=torch.bfloat16, device=DEV)
+    values, stats = attn.attn_probe_softmax_issue(ops, True, kind, 200, wg)
+    torch.cuda.synchronize()
+    x = ((np.arange(64)[:, None] + 64 * np.arange(32)[None, :]) / 256.0 - 8.0).astype(np.float32)
+    ref = np.exp2(x.astype(np.float64))
+    rel = np.abs(values.cpu().numpy().astype(np.float64) - ref) / ref
+    poly = np.zeros((64, 32), dtype=bool)
+    if kind == 2:
+        poly[:] = True
+    elif kind == 3:
+        poly[:, (np.arange(32) % 8) < 2] = True
+    assert rel[~poly].max(initial=0.0) <= 2e-6
+    assert rel[poly].max(initial=0.0) <= 1e-4
+    st = stats.cpu()
+    assert (st[:, 0] > 0).all() and (st[:, 1] > 0).all() and (st[:, 2] > 0).all()
