@@ -134,49 +134,93 @@ def make_step(w, x, dev):
             attn.attn_varlen_plan(cu, cu, ms, ms, w.causal, out=plan)
             attn.attn_fwd_varlen(q, k, v, cu, cu, ms, ms, w.scale, w.causal, out=out, lse=lse,
                                  seq_order=plan)
+            return out, lse
     elif w.sparse:
         bm = x["block_mask"].to(dev)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
 
         def step():
             attn.attn_fwd_blocksparse(q, k, v, bm, w.scale, w.causal, out=out, lse=lse)
+            return out, lse
     else:
         sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
 
         def step():
             attn.attn_fwd(q, k, v, w.scale, w.causal, sl, out=out, lse=lse)
+            return out, lse
     return step
 
 
 def cpu_baseline(w, x, target_s: float):
-    """Time the oracle on whole heads until about target_s seconds have passed."""
+    """Time the oracle on whole heads until about target_s seconds have passed.
+
+    A head is a (batch, query head) pair, or a (sequence, query head) pair of a
+    packed batch; each is the oracle's plain fp64 computation of that head
+    (attention_head, with the block mask's element pattern for the
+    block-sparse workload).  Heads are visited in a seeded random order and
+    run `workers` at a time; the rate is the visited heads' algorithmic FLOPs
+    over the wall time.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     from oracle.attention import default_workers
 
     workers = default_workers()
-    if w.varlen or w.sparse:
-        return None
     q = x["q"].float().numpy()
     k = x["k"].float().numpy()
     v = x["v"].float().numpy()
-    sl = None if x["seqlens_k"] is None else x["seqlens_k"].numpy()
-    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    G = w.Hq // w.Hkv
     rng = np.random.default_rng(w.seed)
+    if w.varlen:
+        cu = x["cu_seqlens_q"].numpy()
+        heads = [(z, h) for z in range(len(cu) - 1) for h in range(w.Hq)]
+
+        def one(zh):
+            z, h = zh
+            a, e = int(cu[z]), int(cu[z + 1])
+            oracle.attention_head(q[a:e, h], k[a:e, h // G], v[a:e, h // G], w.scale, w.causal)
+            L = e - a
+            f = 2.0 * L * L * (w.d + w.d_v)
+            return f / 2.0 if w.causal else f
+    else:
+        sl = None if x.get("seqlens_k") is None else x["seqlens_k"].numpy()
+        allowed = None
+        if w.sparse:
+            allowed = oracle.block_mask_to_elements(x["block_mask"][0].numpy(), w.N, w.N,
+                                                    inputs.SPARSE_BLOCK, inputs.SPARSE_BLOCK)
+        heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+        per_head = algorithmic_flops(w, x) / (w.B * w.Hq)
+
+        def one(bh):
+            b, h = bh
+            nk = None if sl is None else int(sl[b])
+            oracle.attention_head(q[b, :, h], k[b, :, h // G], v[b, :, h // G], w.scale, w.causal,
+                                  nk, allowed=allowed)
+            return per_head
     rng.shuffle(heads)
-    done, t_total, pos = 0, 0.0, 0
-    while pos < len(heads) and t_total < target_s:
-        chunk = heads[pos:pos + workers]
-        t0 = time.perf_counter()
-        oracle.attention_forward(q, k, v, w.scale, w.causal, sl, workers=workers, heads=chunk)
-        t_total += time.perf_counter() - t0
-        done += len(chunk)
-        pos += len(chunk)
-    flops_per_head = algorithmic_flops(w, x) / (w.B * w.Hq)
-    return {"value": flops_per_head * done / t_total / 1e12, "unit": "TFLOP/s", "cores": workers,
-            "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs of {w.name}, fp64 NumPy with S "
-                      f"and P materialised, {workers} threads, {t_total:.1f} s wall"}
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - threadpoolctl is present in this image
+        threadpool_limits = None
+    done, flop, t_total, pos = 0, 0.0, 0.0, 0
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        while pos < len(heads) and t_total < target_s:
+            chunk = heads[pos:pos + workers]
+            t0 = time.perf_counter()
+            if threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    flop += sum(ex.map(one, chunk))
+            else:
+                flop += sum(ex.map(one, chunk))
+            t_total += time.perf_counter() - t0
+            done += len(chunk)
+            pos += len(chunk)
+    kind = "(sequence, head)" if w.varlen else "(batch, head)"
+    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} {kind} pairs of {w.name}, fp64 NumPy with S and P "
+                      f"materialised, {workers} threads, {t_total:.1f} s wall"}
 
 
 def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
@@ -257,6 +301,47 @@ def softmax_issue(dev, budget_us: int = 20000, seed: int = 7):
     return out
 
 
+def compare_builds(w, x, dev, libs, steps: int, rounds: int, which: str = "fwd"):
+    """TFLOP/s of the workload's step under each library build, in interleaved rounds in one process.
+
+    Each round times `steps` steps under every build in turn (after 3 untimed
+    steps), so clock and temperature drift affect every build alike.  Returns
+    per build the mean, min and max over the rounds, the change of the mean
+    against the first build, and whether its outputs equal the first build's
+    bit for bit.  which = "bwd" times the backward (FLOPs 2.5x the forward's).
+    """
+    flops = algorithmic_flops(w, x) * (2.5 if which == "bwd" else 1.0)
+    res = {lib: [] for lib in libs}
+    outs = {}
+    for rnd in range(rounds):
+        for lib in libs:
+            with attn.using_library(os.path.abspath(lib)):
+                step = make_bwd_step(w, x, dev) if which == "bwd" else make_step(w, x, dev)
+                if rnd == 0:
+                    outs[lib] = [t.clone() for t in step()]
+                for _ in range(3):
+                    step()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    step()
+                e1.record()
+                torch.cuda.synchronize()
+                res[lib].append(flops / (e0.elapsed_time(e1) / steps * 1e-3) / 1e12)
+        print(f"[bench] compare round {rnd}: " +
+              " ".join(f"{os.path.basename(l)}={res[l][-1]:.1f}" for l in libs), file=sys.stderr,
+              flush=True)
+    base = float(np.mean(res[libs[0]]))
+    return {os.path.basename(l): {"tflops_mean": round(float(np.mean(r)), 1),
+                                  "min": round(float(np.min(r)), 1),
+                                  "max": round(float(np.max(r)), 1),
+                                  "vs_first_pct": round((float(np.mean(r)) / base - 1) * 100, 2),
+                                  "bitwise_equal_first": all(
+                                      torch.equal(a, b) for a, b in zip(outs[l], outs[libs[0]]))}
+            for l, r in res.items()}
+
+
 def warm_up(step, n):
     """Runs n untimed warm-up steps; returns the first one's time in ms (cold caches), or None."""
     if n <= 0:
@@ -277,33 +362,7 @@ def bench_backward(args, w, x, dev, fwd_flops):
     if w.sparse or w.d not in (64, 128) or w.d_v != w.d:
         print("the backward covers the dense workloads with d = 64 or 128", file=sys.stderr)
         sys.exit(2)
-    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
-    do = inputs.make_dout(x["q"].shape, w.seed + 77).to(dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    lib = attn.load_library()
-    if w.varlen:
-        # packed: the LPT plan and the backward, as the forward's step runs plan + forward
-        cq, ck, mx = x["cu_seqlens_q"].to(dev), x["cu_seqlens_k"].to(dev), x["max_seqlen"]
-        order = torch.empty((cq.numel() - 1,), dtype=torch.int32, device=dev)
-        attn.attn_varlen_plan(cq, ck, mx, mx, w.causal, out=order)
-        o, lse = attn.attn_fwd_varlen(q, k, v, cq, ck, mx, mx, w.scale, w.causal, seq_order=order)
-        ws = torch.empty((lib.attn_bwd_workspace_size(1, w.Hq, q.shape[0]),), dtype=torch.uint8,
-                         device=dev)
-
-        def step():
-            attn.attn_varlen_plan(cq, ck, mx, mx, w.causal, out=order)
-            attn.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, mx, mx, w.scale, w.causal,
-                                 seq_order=order, workspace=ws, out=(dq, dk, dv))
-    else:
-        sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
-        o, lse = attn.attn_fwd(q, k, v, w.scale, w.causal, sl)
-        ws = torch.empty((lib.attn_bwd_workspace_size(w.B, w.Hq, w.N),), dtype=torch.uint8,
-                         device=dev)
-
-        def step():
-            attn.attn_bwd(q, k, v, o, lse, do, w.scale, w.causal, sl, workspace=ws,
-                          out=(dq, dk, dv))
-
+    step = make_bwd_step(w, x, dev)
     first_ms = warm_up(step, args.warmup)
     K = args.steps
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -335,6 +394,43 @@ def bench_backward(args, w, x, dev, fwd_flops):
     print(json.dumps(line), flush=True)
 
 
+def make_bwd_step(w, x, dev):
+    """One backward call (attn_bwd, or the LPT plan and attn_bwd_varlen) on the workload.
+
+    The forward's O and LSE are computed once here; the step returns the
+    (dq, dk, dv) output tensors it writes.
+    """
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    do = inputs.make_dout(x["q"].shape, w.seed + 77).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lib = attn.load_library()
+    if w.varlen:
+        # packed: the LPT plan and the backward, as the forward's step runs plan + forward
+        cq, ck, mx = x["cu_seqlens_q"].to(dev), x["cu_seqlens_k"].to(dev), x["max_seqlen"]
+        order = torch.empty((cq.numel() - 1,), dtype=torch.int32, device=dev)
+        attn.attn_varlen_plan(cq, ck, mx, mx, w.causal, out=order)
+        o, lse = attn.attn_fwd_varlen(q, k, v, cq, ck, mx, mx, w.scale, w.causal, seq_order=order)
+        ws = torch.empty((lib.attn_bwd_workspace_size(1, w.Hq, q.shape[0]),), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            attn.attn_varlen_plan(cq, ck, mx, mx, w.causal, out=order)
+            attn.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, mx, mx, w.scale, w.causal,
+                                 seq_order=order, workspace=ws, out=(dq, dk, dv))
+            return dq, dk, dv
+    else:
+        sl = None if x["seqlens_k"] is None else x["seqlens_k"].to(dev)
+        o, lse = attn.attn_fwd(q, k, v, w.scale, w.causal, sl)
+        ws = torch.empty((lib.attn_bwd_workspace_size(w.B, w.Hq, w.N),), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            attn.attn_bwd(q, k, v, o, lse, do, w.scale, w.causal, sl, workspace=ws,
+                          out=(dq, dk, dv))
+            return dq, dk, dv
+    return step
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +447,10 @@ def main():
     ap.add_argument("--library", default=None, metavar="PATH",
                     help="time another build of the library (e.g. "
                          "exact_attention_18_amd/libattn_exp2poly.so) instead of libattn.so")
+    ap.add_argument("--compare", nargs="+", default=None, metavar="LIB",
+                    help="only compare library builds: the workload's TFLOP/s under each, in "
+                         "interleaved rounds in one process (one JSON line)")
+    ap.add_argument("--rounds", type=int, default=4, help="rounds of --compare")
     ap.add_argument("--softmax-issue", action="store_true",
                     help="only measure the issue cost of the softmax's exp2 (hardware or polynomial) "
                          "beside a wave streaming MFMAs (attn_probe_softmax_issue), one JSON line")
@@ -388,6 +488,11 @@ def main():
     x = inputs.workload_inputs(w)
     flops = algorithmic_flops(w, x)
     attn.load_library()
+    if args.compare:
+        cmp_ = compare_builds(w, x, dev, args.compare, args.steps, args.rounds, args.which)
+        print(json.dumps({"compare": cmp_, "workload": w.name, "pass": args.which,
+                          "steps": args.steps, "rounds": args.rounds}), flush=True)
+        return
     if args.which == "bwd":
         return bench_backward(args, w, x, dev, flops)
     step = make_step(w, x, dev)

@@ -93,5 +93,23 @@ def build(verbose: bool = False, extra=(), variants: bool = True) -> str:
     return LIB
 
 
+def build_variant(out: str, defines=(), verbose: bool = False) -> str:
+    """Compile one library with extra -D defines (e.g. ATTN_EXP2_POLY=4) into `out`."""
+    out = os.path.abspath(out)
+    return _finish(out, _compile(out, tuple(f"-D{d}" for d in defines), verbose), verbose)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+
+    ap = argparse.ArgumentParser(description="Build libattn.so and its variants for gfx950.")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="build one variant with this preprocessor define (repeatable)")
+    ap.add_argument("--out", default=None, help="output path of the variant (with --define)")
+    a = ap.parse_args()
+    if a.define:
+        if not a.out:
+            ap.error("--define needs --out")
+        print(build_variant(a.out, a.define, verbose=True))
+    else:
+        print(build(verbose=True))

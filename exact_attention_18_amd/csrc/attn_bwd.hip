@@ -327,8 +327,12 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     {  // K (group 0) and V (group 1) of the block
       TileCopy<kKeysPerWg, D> c;
       const __bf16* src = (grp == 0 ? p.k : p.v) + (ur.k0 + k0) * kv_stride + (long)hkv * D;
-      c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gtid);
-      c.store(kv_t + grp * kKeysPerWg * kRowElems, gtid);
+      // an opaque copy of the thread index: the copy's lane addresses are
+      // recomputed per work item instead of being kept across the loop
+      int gt = gtid;
+      asm volatile("" : "+v"(gt));
+      c.load(src, kv_stride, min(nk - k0, kKeysPerWg), gt);
+      c.store(kv_t + grp * kKeysPerWg * kRowElems, gt);
     }
 
     const int wk0 = k0 + (wave & 3) * 32;  // this wave's first key
@@ -494,13 +498,20 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     constexpr int kRedPitch = D + 4;
     static_assert(sizeof(kv_t) >= kKeysPerWg * kRedPitch * sizeof(float), "reduction buffer");
     float* red = reinterpret_cast<float*>(kv_t);  // K and V are no longer needed
-    const int kl = (wave & 3) * 32 + (lane & 31);   // key within the block
+    // Lane quantities of the reduction and the stores, derived afresh from an
+    // opaque copy of the thread index so that the compiler does not keep them
+    // live across the period loop.
+    int tid_late = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid_late));
+    const int lane_l = tid_late & 63, g_l = lane_l >> 5;
+    const int kl = (wave & 3) * 32 + (lane_l & 31);   // key within the block
+    const int key_l = k0 + kl;
     auto xfer = [&](f32x16* acc, bool add) {
 #pragma unroll
       for (int t = 0; t < TD; ++t)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g);
+          float4* slot = reinterpret_cast<float4*>(red + kl * kRedPitch + 32 * t + 8 * r4 + 4 * g_l);
           if (add) {
             const float4 o = *slot;
             acc[t][4 * r4 + 0] += o.x;
@@ -521,9 +532,9 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     __syncthreads();
     if (grp == 0) xfer(dv_acc, true);
 
-    if (grp == 0 && key < ur.k_write && key < k0 + kKeysPerWg) {
-      __bf16* dkrow = p.dk + (ur.k0 + key) * kv_stride + (long)hkv * D;
-      __bf16* dvrow = p.dv + (ur.k0 + key) * kv_stride + (long)hkv * D;
+    if (grp == 0 && key_l < ur.k_write && key_l < k0 + kKeysPerWg) {
+      __bf16* dkrow = p.dk + (ur.k0 + key_l) * kv_stride + (long)hkv * D;
+      __bf16* dvrow = p.dv + (ur.k0 + key_l) * kv_stride + (long)hkv * D;
 #pragma unroll
       for (int t = 0; t < TD; ++t)
 #pragma unroll
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
             a[e] = (__bf16)(dk_acc[t][4 * r4 + e] * p.scale);
             c[e] = (__bf16)dv_acc[t][4 * r4 + e];
           }
-          const int dcol = 32 * t + 8 * r4 + 4 * g;
+          const int dcol = 32 * t + 8 * r4 + 4 * g_l;
           *reinterpret_cast<bf16x4*>(dkrow + dcol) = a;
           *reinterpret_cast<bf16x4*>(dvrow + dcol) = c;
         }
