@@ -560,24 +560,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   for (j = max(j, 1); j < n_tiles; ++j) step_dynamic(j);
   if (n_tiles > 0 && active(n_tiles - 1)) last_pv(((n_tiles - 1) & 1) ? v_lds1 : v_lds0);
 
-  // ---- epilogue: O = o / l in bf16, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = o / l in bf16, LSE = (m + log2 l) ln 2.  O leaves
+  // through LDS as in the ping-pong kernel: each wave writes its 32 x D block
+  // row-major (16-byte chunk c of row r at c XOR (r % (D/8))) into half of a
+  // K buffer, which no wave reads after the last barrier (the final P V reads
+  // V only), and stores whole rows with 16-byte stores.
+  constexpr int kOChunks = D / 8;
+  static_assert(64 % kOChunks == 0 && kRowsPerWave % (64 / kOChunks) == 0, "O row passes");
+  static_assert(kWaves == 4 && 2 * kRowsPerWave * D <= T::K_ELEMS, "O blocks fit the K buffers");
   const float l_tot = pair_sum(l_run);
-  if (qrow < q_len) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = p.o + (q_row0 + qrow) * q_stride + (long)h * D;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  __bf16* const ost = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * (kRowsPerWave * D);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt)
+  for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 ov;
+    for (int rq = 0; rq < 4; ++rq) {
+      bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * rq + 4 * g) = ov;
-      }
-    if (g == 0)
-      p.lse[lse_base + (long)h * lse_hstride + qrow] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
+      const int chk = (dt * 4 + rq) ^ (l32 % kOChunks);  // columns dt*32 + 8 rq .. +7
+      *reinterpret_cast<bf16x4*>(ost + l32 * D + chk * 8 + 4 * g) = ov;
+    }
+  // the wave's LDS writes precede its reads of other lanes' data
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __bf16* const obase = p.o + (q_row0 + wrow0) * q_stride + (long)h * D;
+  constexpr int kRowsPerPass = 64 / kOChunks;
+  const int cc = lane % kOChunks;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / kRowsPerPass; ++i) {
+    const int r = i * kRowsPerPass + lane / kOChunks;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(ost + r * D + (cc ^ (r % kOChunks)) * 8);
+    if (wrow0 + r < q_len) *reinterpret_cast<u32x4*>(obase + r * q_stride + cc * 8) = ov;
   }
+  if (qrow < q_len && g == 0)
+    p.lse[lse_base + (long)h * lse_hstride + qrow] =
+        l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -602,6 +621,10 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   constexpr int CH = CHK > CHV ? CHK : CHV;
   static_assert(CHK * kPpThreads * 8 == 2 * T::BC * DQK && CHV * kPpThreads * 8 == 2 * T::BC * DV,
                 "tile split");
+  constexpr int kOChunks = DV / 8;  // 16-byte chunks of an O row
+  static_assert(64 % kOChunks == 0 && kRowsPerWave % (64 / kOChunks) == 0, "O row passes");
+  static_assert(2 * kRowsPerWave * DV <= T::K_ELEMS && 2 * kRowsPerWave * DV <= TV::V_ELEMS,
+                "two waves' O blocks fit one K or V buffer");
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[T::K_ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[T::K_ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[TV::V_ELEMS];
@@ -1001,22 +1024,42 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     if (!kForceSafe && grp == 0) barrier();
 
     const float l_tot = pair_sum(l_run);
-    if (qrow < q_len) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      __bf16* orow = p.o + (q_row0 + qrow) * o_stride + (long)h * DV;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // O leaves through LDS.  A lane's accumulator holds 4-column pieces of one
+    // row, so storing it directly scatters every store instruction over 32
+    // rows.  Instead each wave writes its 32 x DV block, normalised, in bf16,
+    // row-major into 8 KB of the K/V buffers (after the last barrier no wave
+    // reads them), then stores whole rows with 16-byte stores.  The 16-byte
+    // chunks of row r sit at chunk index XOR (r % 16), so that neither the
+    // column-wise writes nor the row-wise reads conflict on LDS banks.
+    __bf16* const ost = (wave < 2 ? k_lds0 : wave < 4 ? k_lds1 : wave < 6 ? v_lds0 : v_lds1) +
+                        (wave & 1) * (kRowsPerWave * DV);
 #pragma unroll
-      for (int dt = 0; dt < TV::DT; ++dt)
+    for (int dt = 0; dt < TV::DT; ++dt)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          bf16x4 ov;
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * rq + 4 * g) = ov;
-        }
-      if (g == 0)
-        p.lse[lse_base + (long)h * lse_hstride + qrow] =
-            l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
+        const int chk = (dt * 4 + rq) ^ (l32 % kOChunks);  // columns dt*32 + 8 rq .. +7
+        *reinterpret_cast<bf16x4*>(ost + l32 * DV + chk * 8 + 4 * g) = ov;
+      }
+    // the wave's LDS writes precede its reads of other lanes' data
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __bf16* const obase = p.o + (q_row0 + wrow0) * o_stride + (long)h * DV;
+    constexpr int kRowsPerPass = 64 / kOChunks;
+    const int cc = lane % kOChunks;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave / kRowsPerPass; ++i) {
+      const int r = i * kRowsPerPass + lane / kOChunks;
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(ost + r * DV + (cc ^ (r % kOChunks)) * 8);
+      if (wrow0 + r < q_len) *reinterpret_cast<u32x4*>(obase + r * o_stride + cc * 8) = ov;
     }
+    if (qrow < q_len && g == 0)
+      p.lse[lse_base + (long)h * lse_hstride + qrow] =
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   };
 
   // Paired items: workgroup w of XCD x (w = x + 8 m) runs, within that XCD's
