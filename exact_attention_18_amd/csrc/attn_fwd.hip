@@ -107,6 +107,8 @@ struct Tile {
 };
 
 constexpr float kTau = 8.0f;  // conditional-rescale threshold, log2 units
+// Iteration kinds of the d = 64 kernel (which parts are fixed at compile time).
+constexpr int kGeneric = 0, kSteady = 1, kFirst = 2, kLast = 3;
 constexpr float kTwoPowTau = 256.0f;  // 2^kTau
 
 // Race check.  A library built with -DATTN_FORCE_SAFE=1 keeps every
@@ -417,14 +419,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
         if (!vis) sv[kt][r] = -INFINITY;
       }
   };
-  // One iteration.  vb: LDS tile of V_{j-1}; kb: LDS tile of K_{j+1}.  FAST
-  // (compile-time) is the steady state: a predecessor and an active successor
-  // exist and tile j needs no mask, so every predicate folds to true.
-  auto iteration = [&](int j, const __bf16* vb, const __bf16* kb, auto fast_tag) __attribute__((always_inline)) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    const bool do_pv = FAST || (j >= 1 && active(j - 1));
-    const bool do_sm = FAST || active(j);
-    const bool do_s = FAST || (j + 1 < n_tiles && active(j + 1));
+  // One iteration.  vb: LDS tile of V_{j-1}; kb: LDS tile of K_{j+1}.  The
+  // kind (compile-time) fixes which parts run:
+  //   kSteady: a predecessor and an active successor exist and tile j needs
+  //     no mask, so every predicate folds to true;
+  //   kFirst: j = 0 with an active successor (no P V);
+  //   kLast: tile j is active and needs no mask, its predecessor exists, its
+  //     successor does not (no scores);
+  //   kGeneric: every predicate at run time.
+  // kFirst and kGeneric mask tile j when it needs it.
+  auto iteration = [&](int j, const __bf16* vb, const __bf16* kb, auto kind_tag) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    constexpr bool FAST = KIND == kSteady || KIND == kLast;  // no mask
+    const bool do_pv = KIND == kSteady || KIND == kLast || (KIND == kGeneric && j >= 1 && active(j - 1));
+    const bool do_sm = KIND != kGeneric || active(j);
+    const bool do_s = KIND == kSteady || KIND == kFirst ||
+                      (KIND == kGeneric && j + 1 < n_tiles && active(j + 1));
     if (!FAST && do_sm && needs_mask(j)) apply_mask(j);
     float m0 = -INFINITY, m1 = -INFINITY;
     float ls[2] = {0.f, 0.f};
@@ -516,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
 
   // ---- iterations.  Iteration j loads K_{j+2} into the tile K_j used and
   // V_j into the tile V_{j-2} used, reads V_{j-1} and K_{j+1}.
-  auto step_static = [&](int j, auto par, auto fast_tag) __attribute__((always_inline)) {
+  auto step_static = [&](int j, auto par, auto kind_tag) __attribute__((always_inline)) {
     constexpr bool P = decltype(par)::value;  // parity of j
     __bf16* kw = P ? k_lds1 : k_lds0;
     __bf16* vw = P ? v_lds1 : v_lds0;
@@ -528,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    iteration(j, vr, kr, fast_tag);
+    iteration(j, vr, kr, kind_tag);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -540,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    iteration(j, P ? v_lds0 : v_lds1, P ? k_lds0 : k_lds1, std::false_type{});
+    iteration(j, P ? v_lds0 : v_lds1, P ? k_lds0 : k_lds1, std::integral_constant<int, kGeneric>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -550,14 +560,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   // all waves agree on the barrier count.
   int j_hi = 1;
   while (j_hi + 1 < n_tiles && active(j_hi + 1) && !needs_mask(j_hi)) ++j_hi;
-  if (n_tiles > 0) step_dynamic(0);
+  // The first iteration, and the workgroup's last one where this wave is
+  // active there and the tile is unmasked, run with compile-time buffers and
+  // parts; the other iterations past the steady range (masked tiles, waves
+  // whose rows end earlier, single-tile items) run generic.
+  if (n_tiles > 1 && active(1)) {
+    step_static(0, std::false_type{}, std::integral_constant<int, kFirst>{});
+  } else if (n_tiles > 0) {
+    step_dynamic(0);
+  }
   int j = 1;
   for (; j + 1 < j_hi; j += 2) {
-    step_static(j, std::true_type{}, std::true_type{});
-    step_static(j + 1, std::false_type{}, std::true_type{});
+    step_static(j, std::true_type{}, std::integral_constant<int, kSteady>{});
+    step_static(j + 1, std::false_type{}, std::integral_constant<int, kSteady>{});
   }
-  if (j < j_hi) step_static(j++, std::true_type{}, std::true_type{});
-  for (j = max(j, 1); j < n_tiles; ++j) step_dynamic(j);
+  if (j < j_hi) step_static(j++, std::true_type{}, std::integral_constant<int, kSteady>{});
+  for (j = max(j, 1); j < n_tiles - 1; ++j) step_dynamic(j);
+  if (j == n_tiles - 1 && j >= 1) {
+    if (!active(j) || needs_mask(j)) step_dynamic(j);
+    else if (j & 1) step_static(j, std::true_type{}, std::integral_constant<int, kLast>{});
+    else step_static(j, std::false_type{}, std::integral_constant<int, kLast>{});
+  }
   if (n_tiles > 0 && active(n_tiles - 1)) last_pv(((n_tiles - 1) & 1) ? v_lds1 : v_lds0);
 
   // ---- epilogue: O = o / l in bf16, LSE = (m + log2 l) ln 2.  O leaves
