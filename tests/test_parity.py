@@ -77,6 +77,30 @@ def test_small_shapes_full_oracle(B, Nq, Nk, Hq, Hkv, d, causal, padded):
         assert (o_np[empty] == 0).all()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_tiles", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("tail", [0, 17])
+def test_key_tile_counts_full_oracle(d, causal, n_tiles, tail):
+    """Every key-tile count from one to six, whole and ragged.
+
+    A 64-key tile count of n puts the last tile at either parity of the
+    double-buffered loop, and one or two tiles leave no steady-state
+    iteration; a ragged tail masks the last tile.  Nq = 130 adds a query
+    block whose waves hold no rows.
+    """
+    Nk = 64 * (n_tiles - 1) + (tail if tail else 64)
+    Nq = 130
+    seed = 7300 + 17 * n_tiles + tail + d + int(causal)
+    q, k, v = inputs.make_qkv(2, Nq, Nk, 2, 1, d, seed, q_mult=2.0)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[parity] tile counts Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
+    o, lse = _run(q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.attention_forward(to_np64(q), to_np64(k), to_np64(v), scale, causal,
+                                              None, workers=8)
+    assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "small")
+
+
 ASYM = [
     # B, Nq, Nk, Hq, Hkv, causal, padded  (d_qk = 192, d_v = 128)
     (1, 300, 300, 4, 4, True, False),
