@@ -532,9 +532,21 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     __syncthreads();
     if (grp == 0) xfer(dv_acc, true);
 
-    if (grp == 0 && key_l < ur.k_write && key_l < k0 + kKeysPerWg) {
-      __bf16* dkrow = p.dk + (ur.k0 + key_l) * kv_stride + (long)hkv * D;
-      __bf16* dvrow = p.dv + (ur.k0 + key_l) * kv_stride + (long)hkv * D;
+    // dK and dV leave through LDS (the Q and dO tiles are no longer read): a
+    // lane's accumulators hold 4-column pieces of one key row, so storing
+    // them directly scatters every store instruction over 32 rows.  Each wave
+    // of group 0 writes its 32 keys' rows, in bf16, row-major (16-byte chunk c
+    // of row r at chunk c XOR (r % (D/8))) into its part of the Q tiles (dK)
+    // and the dO tiles (dV), then stores whole rows with 16-byte stores.
+    if (grp == 0) {
+      constexpr int kOChunks = D / 8;
+      static_assert(64 % kOChunks == 0 && 32 % (64 / kOChunks) == 0, "row passes");
+      static_assert(sizeof(q_t) >= 4 * 32 * D * sizeof(__bf16) &&
+                        sizeof(do_t) >= 4 * 32 * D * sizeof(__bf16),
+                    "dK, dV staging");
+      const int l32 = lane_l & 31;
+      __bf16* const sk = &q_t[0][0][0] + (wave & 3) * (32 * D);
+      __bf16* const sd = &do_t[0][0][0] + (wave & 3) * (32 * D);
 #pragma unroll
       for (int t = 0; t < TD; ++t)
 #pragma unroll
@@ -545,10 +557,29 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
             a[e] = (__bf16)(dk_acc[t][4 * r4 + e] * p.scale);
             c[e] = (__bf16)dv_acc[t][4 * r4 + e];
           }
-          const int dcol = 32 * t + 8 * r4 + 4 * g_l;
-          *reinterpret_cast<bf16x4*>(dkrow + dcol) = a;
-          *reinterpret_cast<bf16x4*>(dvrow + dcol) = c;
+          const int off = l32 * D + (((t * 4 + r4) ^ (l32 % kOChunks)) * 8) + 4 * g_l;
+          *reinterpret_cast<bf16x4*>(sk + off) = a;
+          *reinterpret_cast<bf16x4*>(sd + off) = c;
         }
+      // the wave's LDS writes precede its reads of other lanes' data
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int wkey0 = k0 + (wave & 3) * 32;  // this wave's first key
+      const long row0 = (ur.k0 + wkey0) * kv_stride + (long)hkv * D;
+      constexpr int kRowsPerPass = 64 / kOChunks;
+      const int cc = lane_l % kOChunks;
+#pragma unroll
+      for (int i = 0; i < 32 / kRowsPerPass; ++i) {
+        const int r = i * kRowsPerPass + lane_l / kOChunks;
+        const int off = r * D + (cc ^ (r % kOChunks)) * 8;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + off);
+        const u32x4 c = *reinterpret_cast<const u32x4*>(sd + off);
+        if (wkey0 + r < ur.k_write && wkey0 + r < k0 + kKeysPerWg) {
+          *reinterpret_cast<u32x4*>(p.dk + row0 + r * kv_stride + cc * 8) = a;
+          *reinterpret_cast<u32x4*>(p.dv + row0 + r * kv_stride + cc * 8) = c;
+        }
+      }
     }
   });
 }
@@ -574,6 +605,9 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
   constexpr int KS = D / 16;  // 16-deep d slices of S^T and dP^T
   __shared__ __attribute__((aligned(1024))) __bf16 k_t[4][kDqTile * kRowElems];
   __shared__ __attribute__((aligned(1024))) __bf16 v_t[2][kDqTile * kRowElems];
+  // Each wave's dQ rows on their way to HBM (see the end of an item).
+  constexpr int kWaves = kBwPpThreads / 64;
+  __shared__ __attribute__((aligned(1024))) __bf16 dq_lds[kWaves * 32 * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -754,17 +788,38 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     if (j + 2 <= n_tiles) period(j + 2, std::integral_constant<int, 2>{});
     if (grp == 0) barrier();
 
-    if (qrow < nq) {
-      __bf16* row = p.dq + qoff;
+    // dQ leaves through LDS: a lane's accumulator holds 4-column pieces of one
+    // row, so storing it directly scatters every store instruction over 32
+    // rows.  Each wave writes its 32 x D block, scaled, in bf16, row-major into
+    // its own part of dq_lds (16-byte chunk c of row r at chunk c XOR (r %
+    // (D/8)), conflict-free for the column writes and the row reads), then
+    // stores whole rows with 16-byte stores.
+    constexpr int kOChunks = D / 8;
+    static_assert(64 % kOChunks == 0 && 32 % (64 / kOChunks) == 0, "dQ row passes");
+    const int l32 = lane & 31;
+    __bf16* const ost = dq_lds + wave * (32 * D);
 #pragma unroll
-      for (int t = 0; t < TD; ++t)
+    for (int t = 0; t < TD; ++t)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          bf16x4 a;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 a;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[t][4 * r4 + e] * p.scale);
-          *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * r4 + 4 * g) = a;
-        }
+        for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[t][4 * r4 + e] * p.scale);
+        const int chk = (t * 4 + r4) ^ (l32 % kOChunks);  // columns 32 t + 8 r4 .. +7
+        *reinterpret_cast<bf16x4*>(ost + l32 * D + chk * 8 + 4 * g) = a;
+      }
+    // the wave's LDS writes precede its reads of other lanes' data
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __bf16* const dq0 = p.dq + (ur.q0 + wrow0) * q_stride + (long)h * D;
+    constexpr int kRowsPerPass = 64 / kOChunks;
+    const int cc = lane % kOChunks;
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPerPass; ++i) {
+      const int r = i * kRowsPerPass + lane / kOChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ost + r * D + (cc ^ (r % kOChunks)) * 8);
+      if (wrow0 + r < nq) *reinterpret_cast<u32x4*>(dq0 + r * q_stride + cc * 8) = v;
     }
   });
 }
