@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
   constexpr int kS = T::KT * T::KS;       // score slices (one K operand each)
   constexpr int kSlices = kPv + kS;
   constexpr int kDecide = kPv / 2;        // first slice of P V key block 1
-  constexpr int kAhead = 2;               // LDS read lookahead, in slices
+  constexpr int kAhead = 3;               // LDS read lookahead, in slices
   static_assert(T::KT == 2 && kDecide >= 2 && 32 % kDecide == 0, "slice plan");
   auto load_operand = [&](int sl, const __bf16* vb, const __bf16* kb) __attribute__((always_inline)) -> bf16x8 {
     if (sl < kPv) {
