@@ -289,6 +289,9 @@ def test_reruns_are_bitwise_identical():
     (1, 700, 16, 2, True, True),     # 8 heads per workgroup, key padding
     (2, 517, 6, 3, True, False),     # 2 heads per workgroup
     (1, 300, 12, 4, False, False),   # 1 head per workgroup (G = 3), non-causal
+    (1, 600, 12, 2, True, False),    # G = 6: 2 heads per workgroup, 3 workgroups per row block
+    (1, 520, 12, 1, True, True),     # G = 12: 4 heads per workgroup, 3 per row block, padding
+    (1, 777, 16, 1, False, False),   # G = 16: 8 heads per workgroup, 2 per row block
 ])
 def test_grouped_heads_equal_repeated_kv_heads_bitwise(B, N, Hq, Hkv, causal, padded):
     """GQA (h_kv = h_q // G) is MHA with each K/V head repeated G times.
