@@ -36,6 +36,10 @@
 //   order (the determinism concern of FlashAttention-4 (papercache summary),
 //   section 3.2.4).
 //
+// Both kernels write their gradients through LDS (each wave's rows there,
+// then whole rows to HBM, 16 bytes per lane) rather than as the 8-byte
+// pieces of 32 rows their accumulator layouts hold.
+//
 // Head dimensions 64 and 128 (template parameter D of every kernel).  LDS
 // tiles hold rows of D bf16 in groups of 16 rows, each row starting
 // at a staggered 16-byte unit of its group (the layout is described at

@@ -46,7 +46,14 @@
 //   The decision is per wavefront (a ballot), so the skip is a uniform branch.
 //   The final O / l and LSE = m + log2 l stay exact.
 // * Softmax runs in the exp2 domain with scale*log2(e) folded into one FMA per
-//   score; LSE is converted back to natural log in the epilogue.
+//   score; LSE is converted back to natural log in the epilogue.  The d = 128
+//   kernel takes a tile's exponentials against the running max first and
+//   computes the row maxima only when some lane's partial sum shows that the
+//   rescale might fire (a sum above 2^tau); the results are those of the
+//   max-first step bit for bit.
+// * O leaves through LDS: each wave writes its normalised rows there and
+//   stores them whole, 16 bytes per lane, instead of the 8-byte pieces of 32
+//   rows that its accumulator layout holds.
 // * Causal: key blocks past the query block's last row are never visited;
 //   masks are applied only on blocks that cross the diagonal or the key tail.
 // * Grid order (decode_work): (batch or sequence, KV head) units are dealt
@@ -69,9 +76,10 @@
 //   the CDNA form of the ping-pong of FlashAttention-4 (papercache summary),
 //   section 3.1.2.  One workgroup barrier per half period.  K/V tiles move
 //   global -> VGPRs -> LDS (16-byte loads, one tile per group per period,
-//   double-buffered), the LDS stores spread over the MFMA phase.  Outside
-//   the block-sparse form a workgroup runs two query blocks of one unit, the
-//   i-th longest and the i-th shortest, back to back.
+//   double-buffered), the LDS stores spread over the MFMA phase.  When a
+//   unit has an even number of query blocks and at most 8192 keys (and the
+//   launch is not block-sparse) a workgroup runs two of them, the i-th
+//   longest and the i-th shortest, back to back.
 // * d = 64: attn_fwd_kernel, 4 waves / 128 query rows per workgroup, each
 //   wave interleaving its own softmax with its MFMAs slice by slice; K/V tiles
 //   move global -> LDS directly (buffer_load ... lds), K two tiles ahead.
