@@ -14,12 +14,14 @@ roofline    : the forward kernel against the dense bf16 MFMA peak of MI355X
               (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU); its
               duration is the mean of per-launch HIP events recorded on the
               launch stream inside the timed region.
-mfma_sustained: what the matrix cores sustain on this device with the
-              forward's instruction and nothing else (attn_probe_mfma), for
-              random and for zero operands, with the shader clock each ran at;
-              the chip lowers its clock under matrix-core load, so the published
-              peak is not reachable with random data.  shape_16x16x32 holds the
-              same for the 16x16x32 MFMA, which the chip runs at a higher clock.
+mfma_sustained: what the matrix cores sustain on this device with one MFMA
+              shape and nothing else (attn_probe_mfma), for random and for
+              zero operands, with the shader clock each ran at; the chip lowers
+              its clock under matrix-core load, so the published peak is not
+              reachable with random data.  The top level holds 32x32x16,
+              shape_16x16x32 the 16x16x32 MFMA (a higher clock);
+              forward_frac_of_random relates the forward to the random-operand
+              rate of the shape it runs on (forward_mfma_shape).
 cpu_baseline: the CPU oracle as it stands, timed on this host on a bounded
               sample of heads of the same workload (heads are independent and
               equal in cost, so the rate is the workload's rate).
@@ -227,9 +229,10 @@ def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
     """Sustained bf16 matrix-core rate of this device, with and without operand bits.
 
     attn_probe_mfma streams one MFMA shape over a full grid laid out as the
-    forward's (one 8-wave workgroup per CU) with no other work: the forward's
-    32x32x16 (the "random" and "zeros" entries) and, for comparison, 16x16x32
-    (the "shape_16x16x32" entry).  Random operands (uniform in [-1, 1), as
+    forward's (one 8-wave workgroup per CU) with no other work: 32x32x16 (the
+    "random" and "zeros" entries; the d = 64, block-sparse and (192, 128)
+    kernels) and 16x16x32 (the "shape_16x16x32" entry; the dense d = 128
+    kernel).  Random operands (uniform in [-1, 1), as
     bf16) give the rate the forward's data allows; zeros give the power-light
     bound.  The shader clock is the mean over waves of s_memtime ticks /
     s_memrealtime ticks x 100 MHz.
@@ -525,7 +528,11 @@ def main():
     if not args.no_mfma_probe:
         print("[bench] sustained matrix-core rate (attn_probe_mfma)", file=sys.stderr, flush=True)
         probe = mfma_sustained(dev)
-        probe["forward_frac_of_random"] = round(achieved / probe["random"]["tflops"], 4)
+        # the dense d = 128 forward runs on 16x16x32 MFMAs; the others on 32x32x16
+        shape16 = w.d == 128 and w.d_v == 128 and w.sparse_window < 0
+        probe["forward_mfma_shape"] = "16x16x32" if shape16 else "32x32x16"
+        ref = probe["shape_16x16x32"]["random"] if shape16 else probe["random"]
+        probe["forward_frac_of_random"] = round(achieved / ref["tflops"], 4)
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

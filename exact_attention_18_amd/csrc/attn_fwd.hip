@@ -30,6 +30,17 @@
 //   A operand of V^T is assembled from two gfx950 transpose reads
 //   (ds_read_b64_tr_b16): in every 16-lane block, lane j addresses 4
 //   consecutive d of key row j/4 and lane i receives the 4 keys of column i.
+// * The dense d = 128 kernel runs both contractions on v_mfma_f32_16x16x32_bf16
+//   instead (a higher sustained clock under the chip's power limit).  A wave's
+//   32 query rows are then two 16-row blocks qb, and lane l holds rows
+//   16 qb + l%16 with keys 16 kb + 4 (l/16) .. +3 of every 16-key block kb, so
+//   row statistics combine lanes l, l^16, l^32 and l^48 (v_permlane16_swap,
+//   then v_permlane32_swap).  A P V instruction consumes 32 keys: lane group
+//   G = l/16 supplies keys 4G..4G+3 and 16+4G..16+4G+3 of them, in both
+//   operands, its V^T part again two transpose reads.  In odd 4-key groups
+//   the 16-wide d blocks of V are stored pairwise swapped, so the four 16-lane
+//   blocks of such a read (4-key groups G = 0..3) fall on alternate LDS bank
+//   halves.
 // * LDS tile layouts (64 keys per tile).  K: 16-row groups, 16-byte chunk
 //   major -- element offset ((row/16)*(D/8) + chunk)*128 + (row%16)*8 -- so the
 //   32 lanes of a score-operand read touch 32 distinct 16-byte bank groups.
@@ -79,7 +90,8 @@
 //   double-buffered), the LDS stores spread over the MFMA phase.  When a
 //   unit has an even number of query blocks and at most 8192 keys (and the
 //   launch is not block-sparse) a workgroup runs two of them, the i-th
-//   longest and the i-th shortest, back to back.
+//   longest and the i-th shortest, back to back.  Dense launches run it on
+//   16x16x32 MFMAs, block-sparse and (192, 128) ones on 32x32x16.
 // * d = 64: attn_fwd_kernel, 4 waves / 128 query rows per workgroup, each
 //   wave interleaving its own softmax with its MFMAs slice by slice; K/V tiles
 //   move global -> LDS directly (buffer_load ... lds), K two tiles ahead.
@@ -131,6 +143,17 @@ constexpr float kTwoPowTau = 256.0f;  // 2^kTau
 #define ATTN_FORCE_SAFE 0
 #endif
 constexpr bool kForceSafe = ATTN_FORCE_SAFE != 0;
+
+// The dense d = 128 forward on v_mfma_f32_16x16x32_bf16 (1, the default) or
+// on v_mfma_f32_32x32x16_bf16 (0), the shape the block-sparse and (192, 128)
+// kernels always use: with 16x16x32 they would exceed 256 VGPRs and spill.
+// Under the chip's power limit the smaller shape holds a higher clock (fewer
+// accumulator registers read per FLOP), at the price of twice as many MFMA
+// issues and row statistics spread over four lanes instead of two.
+#ifndef ATTN_PP_MFMA16
+#define ATTN_PP_MFMA16 1
+#endif
+constexpr bool kPpMfma16 = ATTN_PP_MFMA16 != 0;
 
 // Exponentials of the d = 128 softmax evaluated on the FMA pipe (exp2_poly)
 // instead of v_exp_f32: this many of the 32 per lane and key tile (0, 4, 8
@@ -641,11 +664,21 @@ constexpr int kPpWaves = 8;
 constexpr int kPpThreads = 64 * kPpWaves;
 constexpr int kPpBr = kPpWaves * kRowsPerWave;  // 256 query rows per workgroup
 
-template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool SPARSE = false>
+template <int DQK, int DV, bool CAUSAL, bool VARLEN, bool SPARSE = false, bool M16 = false>
 __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
   // Q and K rows have DQK elements, V and O rows DV (FlashAttention-4's (192, 128) shape).
   using T = Tile<DQK>;   // key tiles, score slices
   using TV = Tile<DV>;   // value tiles, output blocks
+  // M16: scores and P V on v_mfma_f32_16x16x32_bf16.  A lane then holds two
+  // query rows (16 qb + l%16, qb = 0, 1) and 16 keys of each per tile, whose
+  // row statistics combine the four lanes l, l^16, l^32, l^48.
+  static_assert(!M16 || (DQK % 32 == 0 && DV % 16 == 0), "16x16x32 shapes");
+  constexpr int QB = M16 ? 2 : 1;            // query rows per lane
+  constexpr int KS16 = DQK / 32;             // 32-deep d steps of a 16x16x32 score
+  constexpr int DB16 = DV / 16;              // 16-wide d blocks of a 16x16x32 O^T
+  using SV = std::conditional_t<M16, f32x4, f32x16>;
+  constexpr int NSV = M16 ? 4 * QB : T::KT;      // score accumulators (M16: [key block][row])
+  constexpr int NACC = M16 ? DB16 * QB : TV::DT;  // O^T accumulators (M16: [d block][row])
   // 16-byte chunks per thread per tile (one group of 4 waves moves a tile)
   constexpr int CHK = T::BC * DQK / 8 / (kPpThreads / 2);
   constexpr int CHV = T::BC * DV / 8 / (kPpThreads / 2);
@@ -723,12 +756,24 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
     const int wrow0 = q0 + (chunk % cph) * kRowsPerWave;
     const int qrow = wrow0 + l32;
-    bf16x8 qf[T::KS];
+    // query row qb of this lane (M16; else its one row)
+    auto qrow_of = [&](int qb) __attribute__((always_inline)) {
+      return M16 ? wrow0 + 16 * qb + (lane & 15) : qrow;
+    };
+    bf16x8 qf[T::KS];  // M16: qf[qb * KS16 + s] holds d 32 s + 8 (l/16) .. +7
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
-      qf[ks] = qrow < q_len
-                   ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
-                   : bf16x8{};
+    for (int ks = 0; ks < T::KS; ++ks) {
+      if constexpr (M16) {
+        const int qr = qrow_of(ks / KS16);
+        qf[ks] = qr < q_len ? *reinterpret_cast<const bf16x8*>(qbase + (long)qr * q_stride +
+                                                              (ks % KS16) * 32 + 8 * (lane >> 4))
+                            : bf16x8{};
+      } else {
+        qf[ks] = qrow < q_len
+                     ? *reinterpret_cast<const bf16x8*>(qbase + (long)qrow * q_stride + ks * 16 + 8 * g)
+                     : bf16x8{};
+      }
+    }
     apply_qsign(qf, p.qsign);
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // qf ready before any tile load is in flight
@@ -774,10 +819,15 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       *row = 16 * (c / (16 * (DQK / 8))) + rem16 % 16;
       *colb = (rem16 / 16) * 16;
     };
+    // M16: in odd 4-key groups the 16-wide d blocks are swapped pairwise, so
+    // the four 16-lane blocks of a transpose read (4-key groups G, G+1, ...)
+    // fall on alternate bank halves.
     auto v_slot = [&](int c, int* row, int* colb) __attribute__((always_inline)) {
       const int w = c % (DV / 2);
-      *row = 4 * (c / (DV / 2)) + (w % 8) / 2;
-      *colb = (16 * (w / 8) + 8 * (w % 2)) * 2;
+      const int kg = c / (DV / 2);
+      *row = 4 * kg + (w % 8) / 2;
+      const int blk = M16 ? (w / 8) ^ (kg & 1) : w / 8;
+      *colb = (16 * blk + 8 * (w % 2)) * 2;
     };
     // Group 0 moves V tiles, group 1 K tiles; wave w of a group fills the
     // 1 KB slot runs (i*4 + w%4)*64 .. +63 of the tile (16 bytes per lane).
@@ -818,8 +868,11 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         if (i < nch) *reinterpret_cast<u32x4*>(dst + ((i * 4 + gw) * 64 + lane) * 8) = stage[i];
     };
 
-    const int k_lane = ((l32 >> 4) * (DQK / 8) + g) * 128 + (l32 & 15) * 8;
-    const int v_lane = g * TV::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
+    const int k_lane = M16 ? (lane >> 4) * 128 + (lane & 15) * 8
+                           : ((l32 >> 4) * (DQK / 8) + g) * 128 + (l32 & 15) * 8;
+    const int v_lane = M16 ? (lane >> 4) * TV::QUAD + ((lane & 15) >> 2) * 16 + 4 * (lane & 3)
+                           : g * TV::QUAD + ((lane >> 4) & 1) * 64 + ((lane & 15) >> 2) * 16 + 4 * (lane & 3);
+    const int v_swz = M16 ? ((lane >> 4) & 1) * 64 : 0;  // M16: odd 4-key groups' d-block swap
 
     const float c = p.c;
     // Tiles crossing the key tail or the diagonal (or lying wholly above this
@@ -833,20 +886,25 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       return (kv0 + T::BC > nk) || (CAUSAL && kv0 + T::BC - 1 > wrow0) || !block_visible(tile);
     };
 
-    f32x16 sv[T::KT];
-    u32x4 pv_op[T::KT][2];
-    f32x16 acc[TV::DT];
+    SV sv[NSV];
+    u32x4 pv_op[2][2];  // P^T operands: [key block][half] (M16: [row][32-key step])
+    SV acc[NACC];
 #pragma unroll
-    for (int dt = 0; dt < TV::DT; ++dt) acc[dt] = f32x16{};
+    for (int i = 0; i < NACC; ++i) acc[i] = SV{};
 #pragma unroll
-    for (int kt = 0; kt < T::KT; ++kt) sv[kt] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    float m_use = 0.f;
+    for (int i = 0; i < NSV; ++i) sv[i] = SV{};
+    float m_run[QB], l_run[QB], m_use[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+      m_use[qb] = 0.f;
+    }
 
     // ---- MFMA phase: S_j = K_j Q^T (key blocks interleaved), then O += P_{j-1} V_{j-1}.
-    constexpr int kS = T::KT * T::KS;
-    constexpr int kPv = T::KT * 2 * TV::DT;
+    // slices: one LDS operand each (M16: feeding the MFMAs of both rows)
+    constexpr int kS = M16 ? 4 * KS16 : T::KT * T::KS;
+    constexpr int kPv = M16 ? DB16 * 2 : T::KT * 2 * TV::DT;
     constexpr int kAhead = 3;       // LDS operand reads run this many MFMAs ahead
     constexpr int kMoveFirst = 4;   // tile-store slots inside the MFMA phase
     // 8 slices apart where that fits, else spread evenly over the phase
@@ -859,7 +917,18 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       constexpr int nsl = kS + kPv;
       auto operand = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
         constexpr int i = decltype(I)::value;
-        if constexpr (i < n0) {
+        if constexpr (M16) {
+          if constexpr (i < n0) {
+            constexpr int kb16 = i % 4, ks = i / 4;
+            return *reinterpret_cast<const bf16x8*>(kb + k_lane + (kb16 * (DQK / 8) + 4 * ks) * 128);
+          } else {
+            // keys 32 k2 + 4G .. +3 and 32 k2 + 16 + 4G .. +3 of d block db
+            constexpr int s = i - n0;
+            constexpr int db = s % DB16, k2 = s / DB16;
+            const __bf16* p0 = vb + v_lane + (db % 2 ? -v_swz : v_swz) + 8 * k2 * TV::QUAD + db * 64;
+            return read_tr_pair(p0, p0 + 4 * TV::QUAD);
+          }
+        } else if constexpr (i < n0) {
           constexpr int kt = i % T::KT, ks = i / T::KT;
           return *reinterpret_cast<const bf16x8*>(kb + k_lane + (2 * kt * (DQK / 8) + 2 * ks) * 128);
         } else {
@@ -877,7 +946,20 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         constexpr int i = decltype(I)::value;
         const bf16x8 a = opnd[i % kAhead];
         if constexpr (i + kAhead < nsl) opnd[i % kAhead] = operand(std::integral_constant<int, i + kAhead>{});
-        if constexpr (i < n0) {
+        if constexpr (M16) {
+          if constexpr (i < n0) {
+            constexpr int kb16 = i % 4, ks = i / 4;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              sv[kb16 * QB + qb] = mfma16(a, qf[qb * KS16 + ks], ks == 0 ? SV{} : sv[kb16 * QB + qb]);
+          } else {
+            constexpr int s = i - n0;
+            constexpr int db = s % DB16, k2 = s / DB16;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              acc[db * QB + qb] = mfma16(a, __builtin_bit_cast(bf16x8, pv_op[qb][k2]), acc[db * QB + qb]);
+          }
+        } else if constexpr (i < n0) {
           constexpr int kt = i % T::KT, ks = i / T::KT;
           sv[kt] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : sv[kt]);
         } else {
@@ -893,49 +975,100 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
         }
       });
     };
+    // A key is visible to row qb of this lane when it lies below key_lim[qb]
+    // (and its block is set, block-sparse).  Every score position of a lane is
+    // a compile-time offset from the lane's first key, so the mask is one
+    // compare per score against t = key_lim - kv0 - (lane's first key).
+    int key_lim[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) key_lim[qb] = CAUSAL ? min(nk, qrow_of(qb) + 1) : nk;
     auto apply_mask = [&](int tile) __attribute__((always_inline)) {
       const int kv0 = tile * T::BC;
       const bool bvis = block_visible(tile);
+      if constexpr (M16) {
 #pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt)
+        for (int qb = 0; qb < QB; ++qb) {
+          const int t = bvis ? key_lim[qb] - kv0 - 4 * (lane >> 4) : -1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = bvis && key < nk && (!CAUSAL || key <= qrow);
-          if (!vis) sv[kt][r] = -INFINITY;
+          for (int kb16 = 0; kb16 < 4; ++kb16)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (!(16 * kb16 + r < t)) sv[kb16 * QB + qb][r] = -INFINITY;
         }
+      } else {
+        const int t = bvis ? key_lim[0] - kv0 - 4 * g : -1;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!(kt * 32 + 8 * (r >> 2) + (r & 3) < t)) sv[kt][r] = -INFINITY;
+      }
     };
     // ---- VALU phase: online softmax of S_j -> P_j, O rescale when the max moved.
     // Exponentials of the tile against the running max, packed to bf16 into
     // pv_op; returns this lane's partial row sum in ls0 + ls1.
-    auto exps = [&](float& ls0, float& ls1) __attribute__((always_inline)) {
+    // this lane's partial row sums: ls[qb][0] + ls[qb][1] for row qb
+    auto exps = [&](float (&ls)[QB][2]) __attribute__((always_inline)) {
       auto expo = [](int e, float x) __attribute__((always_inline)) {
         return (e % 8) < kExp2Poly / 4 ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
       };
+      if constexpr (M16) {
+        // P^T operand of 32-key step k2, row qb: keys 4G..4G+3 of key block
+        // 2 k2, then the same of key block 2 k2 + 1
 #pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt)
+        for (int kb16 = 0; kb16 < 4; ++kb16)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float e0 = expo(16 * kt + r, fmaf(sv[kt][r], c, -m_use));
-          const float e1 = expo(16 * kt + r + 1, fmaf(sv[kt][r + 1], c, -m_use));
-          if (kt == 0 && r == 0) {
-            ls0 = e0;
-            ls1 = e1;
-          } else {
-            ls0 += e0;
-            ls1 += e1;
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const float e0 = expo(4 * kb16 + r, fmaf(sv[kb16 * QB + qb][r], c, -m_use[qb]));
+              const float e1 = expo(4 * kb16 + r + 1, fmaf(sv[kb16 * QB + qb][r + 1], c, -m_use[qb]));
+              if (kb16 == 0 && r == 0) {
+                ls[qb][0] = e0;
+                ls[qb][1] = e1;
+              } else {
+                ls[qb][0] += e0;
+                ls[qb][1] += e1;
+              }
+              const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+              uint32_t u = __builtin_bit_cast(uint32_t, pk);
+              asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
+              pv_op[qb][kb16 / 2][(kb16 % 2) * 2 + r / 2] = u;
+            }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float e0 = expo(16 * kt + r, fmaf(sv[kt][r], c, -m_use[0]));
+            const float e1 = expo(16 * kt + r + 1, fmaf(sv[kt][r + 1], c, -m_use[0]));
+            if (kt == 0 && r == 0) {
+              ls[0][0] = e0;
+              ls[0][1] = e1;
+            } else {
+              ls[0][0] += e0;
+              ls[0][1] += e1;
+            }
+            const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+            uint32_t u = __builtin_bit_cast(uint32_t, pk);
+            asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
+            pv_op[kt][r >> 3][(r & 7) >> 1] = u;
           }
-          const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-          uint32_t u = __builtin_bit_cast(uint32_t, pk);
-          asm volatile("" : "+v"(u));  // convert here, not among the next phase's MFMAs
-          pv_op[kt][r >> 3][(r & 7) >> 1] = u;
-        }
-      asm volatile("" : "+v"(ls0), "+v"(ls1));  // keep the sums in this phase
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        asm volatile("" : "+v"(ls[qb][0]), "+v"(ls[qb][1]));  // keep the sums in this phase
+    };
+    // any row of the lane without a running max yet
+    auto no_max_yet = [&]() __attribute__((always_inline)) {
+      bool r = m_run[0] == -INFINITY;
+      if constexpr (QB > 1) r = r || m_run[1] == -INFINITY;
+      return r;
     };
     auto vphase = [&](int j) __attribute__((always_inline)) {
       const int tile = tile_of(j);
       if (needs_mask(tile)) apply_mask(tile);
-      float ls0, ls1;
+      float ls[QB][2];
       // Once every row of the wave has a running max, the exponentials are
       // taken against it first.  A lane's partial sum bounds each of its
       // exponentials, so when no lane's sum exceeds 2^tau no score of the
@@ -944,33 +1077,63 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       // exact step below runs (and decides as before), so the results are
       // bitwise those of that step alone.
       bool done = false;
-      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
-        exps(ls0, ls1);
-        done = __builtin_amdgcn_ballot_w64(ls0 + ls1 > kTwoPowTau) == 0;
+      if (__builtin_amdgcn_ballot_w64(no_max_yet()) == 0) {
+        exps(ls);
+        bool big = ls[0][0] + ls[0][1] > kTwoPowTau;
+        if constexpr (QB > 1) big = big || ls[1][0] + ls[1][1] > kTwoPowTau;
+        done = __builtin_amdgcn_ballot_w64(big) == 0;
       }
       if (!done) {
-        float m0 = -INFINITY, m1 = -INFINITY;
+        float mx[QB];
+        if constexpr (M16) {
 #pragma unroll
-        for (int e = 0; e < 32; e += 4) {
-          m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
-          m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
+          for (int qb = 0; qb < QB; ++qb) {
+            float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+            for (int kb16 = 0; kb16 < 4; kb16 += 2) {
+              m0 = max3f(m0, sv[kb16 * QB + qb][0], sv[kb16 * QB + qb][1]);
+              m0 = max3f(m0, sv[kb16 * QB + qb][2], sv[kb16 * QB + qb][3]);
+              m1 = max3f(m1, sv[(kb16 + 1) * QB + qb][0], sv[(kb16 + 1) * QB + qb][1]);
+              m1 = max3f(m1, sv[(kb16 + 1) * QB + qb][2], sv[(kb16 + 1) * QB + qb][3]);
+            }
+            mx[qb] = pair_max(pair16_max(max3f(m0, m1, -INFINITY))) * c;
+          }
+        } else {
+          float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 32; e += 4) {
+            m0 = max3f(m0, sv[e / 16][e % 16], sv[e / 16][e % 16 + 1]);
+            m1 = max3f(m1, sv[e / 16][e % 16 + 2], sv[e / 16][e % 16 + 3]);
+          }
+          mx[0] = pair_max(max3f(m0, m1, -INFINITY)) * c;
         }
-        const float mx = pair_max(max3f(m0, m1, -INFINITY)) * c;
         // The rescale (new max, alpha, l and O scaled) runs only when some
         // row's max grew by more than tau; the test is wave-uniform, and
         // otherwise alpha would be exactly 1.
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          m_use = (m_new == -INFINITY) ? 0.f : m_new;
-          l_run *= alpha;
+        bool grow = mx[0] > m_run[0] + kTau;
+        if constexpr (QB > 1) grow = grow || mx[1] > m_run[1] + kTau;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-          for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
+          for (int qb = 0; qb < QB; ++qb) {
+            const float m_new = fmaxf(m_run[qb], mx[qb]);
+            const float alpha =
+                (m_run[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+            m_run[qb] = m_new;
+            m_use[qb] = (m_new == -INFINITY) ? 0.f : m_new;
+            l_run[qb] *= alpha;
+            if constexpr (M16) {
+#pragma unroll
+              for (int db = 0; db < DB16; ++db) acc[db * QB + qb] *= alpha;
+            } else {
+#pragma unroll
+              for (int dt = 0; dt < TV::DT; ++dt) acc[dt] *= alpha;
+            }
+          }
         }
-        exps(ls0, ls1);
+        exps(ls);
       }
-      l_run += ls0 + ls1;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb][0] + ls[qb][1];
     };
 
     // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
@@ -1054,8 +1217,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     if (j <= n_iter) period(j, std::integral_constant<int, 0>{});
     if (!kForceSafe && grp == 0) barrier();
 
-    const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float l_tot[QB], inv[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      l_tot[qb] = M16 ? pair_sum(pair16_sum(l_run[qb])) : pair_sum(l_run[qb]);
+      inv[qb] = l_tot[qb] > 0.f ? 1.f / l_tot[qb] : 0.f;
+    }
     // O leaves through LDS.  A lane's accumulator holds 4-column pieces of one
     // row, so storing it directly scatters every store instruction over 32
     // rows.  Instead each wave writes its 32 x DV block, normalised, in bf16,
@@ -1065,16 +1232,31 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     // column-wise writes nor the row-wise reads conflict on LDS banks.
     __bf16* const ost = (wave < 2 ? k_lds0 : wave < 4 ? k_lds1 : wave < 6 ? v_lds0 : v_lds1) +
                         (wave & 1) * (kRowsPerWave * DV);
+    if constexpr (M16) {
+      // lane l: row 16 qb + l%16, columns 16 db + 4 (l/16) .. +3
 #pragma unroll
-    for (int dt = 0; dt < TV::DT; ++dt)
+      for (int db = 0; db < DB16; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 ov;
+        for (int qb = 0; qb < QB; ++qb) {
+          bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
-        const int chk = (dt * 4 + rq) ^ (l32 % kOChunks);  // columns dt*32 + 8 rq .. +7
-        *reinterpret_cast<bf16x4*>(ost + l32 * DV + chk * 8 + 4 * g) = ov;
-      }
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[db * QB + qb][e] * inv[qb]);
+          const int r = 16 * qb + (lane & 15);
+          const int chk = (2 * db + (lane >> 5)) ^ (r % kOChunks);
+          *reinterpret_cast<bf16x4*>(ost + r * DV + chk * 8 + 4 * ((lane >> 4) & 1)) = ov;
+        }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < TV::DT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv[0]);
+          const int chk = (dt * 4 + rq) ^ (l32 % kOChunks);  // columns dt*32 + 8 rq .. +7
+          *reinterpret_cast<bf16x4*>(ost + l32 * DV + chk * 8 + 4 * g) = ov;
+        }
+    }
     // the wave's LDS writes precede its reads of other lanes' data
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1088,9 +1270,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       const u32x4 ov = *reinterpret_cast<const u32x4*>(ost + r * DV + (cc ^ (r % kOChunks)) * 8);
       if (wrow0 + r < q_len) *reinterpret_cast<u32x4*>(obase + r * o_stride + cc * 8) = ov;
     }
-    if (qrow < q_len && g == 0)
-      p.lse[lse_base + (long)h * lse_hstride + qrow] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qr = qrow_of(qb);
+      if (qr < q_len && (M16 ? (lane >> 4) == 0 : g == 0))
+        p.lse[lse_base + (long)h * lse_hstride + qr] =
+            l_tot[qb] > 0.f ? (m_run[qb] + log2f(l_tot[qb])) * kLn2 : -INFINITY;
+    }
   };
 
   // Paired items: workgroup w of XCD x (w = x + 8 m) runs, within that XCD's
@@ -1193,8 +1379,8 @@ int launch_one(Params p, int grid, hipStream_t stream) {
   p.paired = 0;
   if constexpr (use_pp(D)) {
     const int wgs = pp_grid(p, grid, true);
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, D, CAUSAL, VARLEN>), dim3(wgs), dim3(kPpThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<D, D, CAUSAL, VARLEN, false, kPpMfma16>), dim3(wgs),
+                       dim3(kPpThreads), 0, stream, p);
   }
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(kThreads), 0, stream,

@@ -18,6 +18,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -36,6 +37,13 @@ constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for raw 32-b
 // in register r.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16: C[16x16] += A[16x32] B[32x16].  Operand layout:
+// lane l holds row (A) or column (B) l%16 and the 8 k-elements 8*(l/16)..+7;
+// the accumulator: lane l holds column l%16 and rows 4*(l/16) + r in register r.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // max(a, b, c) in one instruction.  fmaxf would make the compiler quiet
@@ -58,6 +66,19 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The same over the lane pair (l, l^16) with v_permlane16_swap, which exchanges
+// the odd 16-lane rows of one register with the even rows of another.
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), -INFINITY);
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
