@@ -829,11 +829,13 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
       const int blk = M16 ? (w / 8) ^ (kg & 1) : w / 8;
       *colb = (16 * blk + 8 * (w % 2)) * 2;
     };
-    // Group 0 moves V tiles, group 1 K tiles; wave w of a group fills the
+    // Group 0 moves K tiles, group 1 V tiles; wave w of a group fills the
     // 1 KB slot runs (i*4 + w%4)*64 .. +63 of the tile (16 bytes per lane).
     // Rows past kv_end read as zero (buffer range check) and are masked.
+    // (The other assignment is as correct, by the same buffer windows, and
+    // measured 0.1-0.7 % slower.)
     const int gw = wave & 3;
-    const bool fetch_v = grp == 0;
+    const bool fetch_v = grp == 1;
     const int nch = fetch_v ? CHV : CHK;  // chunks per lane of this group's tiles
     const uint32_t row_bytes = static_cast<uint32_t>(fetch_v ? v_stride : k_stride) * 2u;
     uint32_t goff[CH];
@@ -1139,10 +1141,14 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     // ---- schedule.  Half periods h = 0, 1, ...: group 0 runs M_j at h = 2j and
     // V_j at h = 2j+1, group 1 runs M_j at h = 2j+1 and V_j at h = 2j+2.  K_t
     // lives in k[t%2], V_t in v[t%2].  Tiles move global -> VGPRs -> LDS:
-    // during M_j, between two MFMAs, group 0 stores V_j (loaded one period
-    // earlier) and group 1 stores K_{j+1}; at the start of V_j (block-sparse:
-    // at the end of M_j) they load V_{j+1} and K_{j+2}.  Each store is complete before the barrier that
-    // ends its phase, which precedes the first read of the tile.
+    // during M_j, between two MFMAs, the V mover (group 1) stores V_j (loaded
+    // one period earlier) and the K mover (group 0) stores K_{j+1}; at the
+    // start of V_j (block-sparse: at the end of M_j) they load V_{j+1} and
+    // K_{j+2}.  Each store is complete before the barrier that ends its phase,
+    // which precedes the first read of the tile.  V_j is written in v[j%2]
+    // during M_j of either group (V_{j-2} there was last read in M_{j-1}) and
+    // first read in M_{j+1}; K_{j+1} in k[(j+1)%2] likewise (K_{j-1} last read
+    // in M_{j-1}, K_{j+1} first read in M_{j+1}).
     constexpr bool kLoadInMfmaPhase = SPARSE;
     auto kbuf = [&](auto I) __attribute__((always_inline)) -> __bf16* {
       if constexpr (decltype(I)::value % 2 == 0) return k_lds0; else return k_lds1;
@@ -1199,7 +1205,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void attn_fwd_pp_kernel(Params p) {
     for (int kt = 0; kt < T::KT; ++kt) pv_op[kt][0] = pv_op[kt][1] = u32x4{};
     for (int i = tid; i < TV::V_ELEMS / 8; i += kPpThreads)
       reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{};
-    // prologue: K_0 stored and K_1 loaded (group 1); V_0 loaded (group 0)
+    // prologue: K_0 stored and K_1 loaded (K mover); V_0 loaded (V mover)
     if (fetch_v) {
       if (n_iter > 0) load_tile_at(tile_of(0));
     } else {
