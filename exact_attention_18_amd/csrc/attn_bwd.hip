@@ -444,6 +444,10 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
         const float* l2t = st_t[grp][B0];
         const float* ddt = st_t[grp][B0] + kQStep;
         const bool full = wk0 + 32 <= nk && (!CAUSAL || wk0 + 31 <= i0);
+        // Row 8 r4 + 4 g + e of the step sees this lane's key when 8 r4 + e
+        // >= u (one compare per score): the key lies below nk and, causal,
+        // not past the row.
+        const int u = key < nk ? (CAUSAL ? key - i0 - 4 * g : INT_MIN) : INT_MAX;
         auto block = [&](bool masked) __attribute__((always_inline)) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
               const int r = 4 * r4 + e;
               const float lv = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
               const float dv_ = e == 0 ? dd.x : e == 1 ? dd.y : e == 2 ? dd.z : dd.w;
-              const bool vis = !masked || (key < nk && (!CAUSAL || key <= i0 + qi + e));
+              const bool vis = !masked || 8 * r4 + e >= u;
               const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -lv)) : 0.f;
               pv[e] = pe;
               dsv[e] = pe * (dp_acc[r] - dv_);
@@ -747,9 +751,11 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
       if (j < n_tiles) {
         const int j0 = j * kDqTile;
         const bool full = j0 + kDqTile <= nk && (!CAUSAL || j0 + kDqTile - 1 <= wrow0);
+        // keys below key_lim are visible to this lane's row; score r of the
+        // lane is key j0 + 4 g + (a compile-time offset): one compare per score
+        const int t = (CAUSAL ? min(nk, qrow + 1) : nk) - j0 - 4 * g;
         auto dsval = [&](int r, bool masked) __attribute__((always_inline)) {
-          const int kk = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = !masked || (kk < nk && (!CAUSAL || kk <= qrow));
+          const bool vis = !masked || 8 * (r >> 2) + (r & 3) < t;
           const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], p.c, -l2)) : 0.f;
           return pe * (dp_acc[r] - dd);
         };

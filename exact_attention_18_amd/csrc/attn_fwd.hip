@@ -439,16 +439,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
       pv_op[kt][r >> 3][(r & 7) >> 1] = u;
     }
   };
+  // Keys below key_lim are visible to this lane's row; each score position
+  // is a compile-time offset from the lane's first key, so the mask is one
+  // compare per score.
+  const int key_lim = CAUSAL ? min(nk, qrow + 1) : nk;
   auto apply_mask = [&](int tile) __attribute__((always_inline)) {
-    const int kv0 = tile * T::BC;
+    const int t = key_lim - tile * T::BC - 4 * g;
 #pragma unroll
     for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool vis = key < nk && (!CAUSAL || key <= qrow);
-        if (!vis) sv[kt][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (!(kt * 32 + 8 * (r >> 2) + (r & 3) < t)) sv[kt][r] = -INFINITY;
   };
   // One iteration.  vb: LDS tile of V_{j-1}; kb: LDS tile of K_{j+1}.  The
   // kind (compile-time) fixes which parts run:
