@@ -513,7 +513,6 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     asm volatile("" : "+v"(tid_late));
     const int lane_l = tid_late & 63, g_l = lane_l >> 5;
     const int kl = (wave & 3) * 32 + (lane_l & 31);   // key within the block
-    const int key_l = k0 + kl;
     auto xfer = [&](f32x16* acc, bool add) {
 #pragma unroll
       for (int t = 0; t < TD; ++t)
