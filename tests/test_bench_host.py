@@ -52,3 +52,17 @@ def test_committed_summaries_record_their_code_and_traffic():
         text = open(f).read()
         assert re.search(r"^kernel_source_sha256: [0-9a-f]{64}$", text, re.M), os.path.basename(f)
         assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M), os.path.basename(f)
+
+
+def test_committed_summaries_describe_the_current_code():
+    """The forward summaries were taken on the kernel code as it stands, so the bench reports traffic."""
+    import glob
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sha = bench.kernel_source_sha256()
+    for f in glob.glob(os.path.join(root, "profiles", "attn_fwd_*.md")):
+        m = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", open(f).read(), re.M)
+        assert m and m.group(1) == sha, os.path.basename(f)
+        w = os.path.basename(f)[len("attn_fwd_"):-len(".md")]
+        assert bench.measured_traffic(w) is not None, w
