@@ -134,8 +134,8 @@ __global__ __launch_bounds__(kProbeThreads, 1) void xcd_probe_kernel(int32_t* __
 // the exponential unit, not the FMA pipes, limits the softmax.  On CDNA4 the
 // exponential issues from the same VALU as an FMA, so the question is what
 // each form costs in VALU issue, with the other wave of the SIMD streaming
-// MFMAs as in the forward's ping-pong.  Waves 0-3 stream the forward's MFMA
-// (or idle); waves 4-7, one per SIMD beside them, run a softmax-shaped loop:
+// MFMAs as in the forward's ping-pong.  Waves 0-3 stream
+// v_mfma_f32_32x32x16_bf16 (or idle); waves 4-7, one per SIMD beside them, run a softmax-shaped loop:
 // per lane and iteration 32 elements, each x = s * c - m (one FMA), e = exp2(x),
 // a running sum, a running max (v_max3 over pairs) and packing pairs to bf16 --
 // the forward's instruction mix.  The exponential is v_exp_f32 (kind 1), the

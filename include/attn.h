@@ -303,8 +303,9 @@ const char* attn_strerror(int status);
  * attention).  The roofline analysis of FlashAttention-4 (papercache
  * summary), section 3.1.1, prices the attention tile in cycles of the matrix
  * core; this call measures what that unit sustains on the device under a full
- * grid, with the forward's instruction (v_mfma_f32_32x32x16_bf16) or the
- * 16x16x32 shape and no other work, so the forward's rate can be compared
+ * grid, with either MFMA shape the forward uses (v_mfma_f32_32x32x16_bf16:
+ * the d = 64, (192, 128) and block-sparse kernels; v_mfma_f32_16x16x32_bf16:
+ * the dense d = 128 kernel) and no other work, so the forward's rate can be compared
  * with it as well as with the published peak.  The clock drops under
  * matrix-core load by an amount that depends on the operand bits, hence the
  * caller-supplied operands.
@@ -338,7 +339,7 @@ int attn_probe_mfma(const void* operands, int shape, int iters, int workgroups, 
  * evaluates part of each row's exp2 as a polynomial on the FMA units because
  * its exponential unit limits the softmax.  This call prices that choice on
  * this device: in each 512-thread workgroup (one per CU, as the forward's),
- * waves 0-3 stream the forward's MFMA (mfma_on = 1) or idle (0), and waves
+ * waves 0-3 stream v_mfma_f32_32x32x16_bf16 (mfma_on = 1) or idle (0), and waves
  * 4-7, one beside each of them on its SIMD, run the forward's softmax
  * instruction mix on 32 elements per lane and iteration (FMA, exp2, running
  * sum, v_max3, bf16 packing).  exp_kind: 0 = those waves idle,
