@@ -230,9 +230,8 @@ def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
 
     attn_probe_mfma streams one MFMA shape over a full grid laid out as the
     forward's (one 8-wave workgroup per CU) with no other work: 32x32x16 (the
-    "random" and "zeros" entries; the d = 64, block-sparse and (192, 128)
-    kernels) and 16x16x32 (the "shape_16x16x32" entry; the dense d = 128
-    kernel).  Random operands (uniform in [-1, 1), as
+    "random" and "zeros" entries; the d = 64 and (192, 128) kernels) and
+    16x16x32 (the "shape_16x16x32" entry; the d = 128 kernel).  Random operands (uniform in [-1, 1), as
     bf16) give the rate the forward's data allows; zeros give the power-light
     bound.  The shader clock is the mean over waves of s_memtime ticks /
     s_memrealtime ticks x 100 MHz.
@@ -528,8 +527,8 @@ def main():
     if not args.no_mfma_probe:
         print("[bench] sustained matrix-core rate (attn_probe_mfma)", file=sys.stderr, flush=True)
         probe = mfma_sustained(dev)
-        # the dense d = 128 forward runs on 16x16x32 MFMAs; the others on 32x32x16
-        shape16 = w.d == 128 and w.d_v == 128 and w.sparse_window < 0
+        # the d = 128 forward runs on 16x16x32 MFMAs; the others on 32x32x16
+        shape16 = w.d == 128 and w.d_v == 128
         probe["forward_mfma_shape"] = "16x16x32" if shape16 else "32x32x16"
         ref = probe["shape_16x16x32"]["random"] if shape16 else probe["random"]
         probe["forward_frac_of_random"] = round(achieved / ref["tflops"], 4)

@@ -455,8 +455,8 @@ def attn_probe_mfma(operands: torch.Tensor, iters: int, workgroups: int,
     """Launch the matrix-core rate probe; returns (sink, clocks) on the device.
 
     operands: bf16 [8, 64, 8] (4 A then 4 B operands, per lane).  shape: 32
-    (32x32x16 MFMA: the d = 64, (192, 128) and block-sparse kernels) or 16
-    (16x16x32: the dense d = 128 kernel).  FLOP per launch is
+    (32x32x16 MFMA: the d = 64 and (192, 128) kernels) or 16 (16x16x32: the
+    d = 128 kernel).  FLOP per launch is
     workgroups * 8 * iters * 16 * 32768 for either shape (probe_flop()).
     clocks[w] = (shader-clock ticks, 100 MHz real-time ticks) of wave w's loop.
     """

@@ -30,8 +30,9 @@
 //   A operand of V^T is assembled from two gfx950 transpose reads
 //   (ds_read_b64_tr_b16): in every 16-lane block, lane j addresses 4
 //   consecutive d of key row j/4 and lane i receives the 4 keys of column i.
-// * The dense d = 128 kernel runs both contractions on v_mfma_f32_16x16x32_bf16
-//   instead (a higher sustained clock under the chip's power limit).  A wave's
+// * The d = 128 kernel (dense and block-sparse launches) runs both
+//   contractions on v_mfma_f32_16x16x32_bf16 instead (a higher sustained
+//   clock under the chip's power limit).  A wave's
 //   32 query rows are then two 16-row blocks qb, and lane l holds rows
 //   16 qb + l%16 with keys 16 kb + 4 (l/16) .. +3 of every 16-key block kb, so
 //   row statistics combine lanes l, l^16, l^32 and l^48 (v_permlane16_swap,
@@ -90,8 +91,8 @@
 //   double-buffered), the LDS stores spread over the MFMA phase.  When a
 //   unit has an even number of query blocks and at most 8192 keys (and the
 //   launch is not block-sparse) a workgroup runs two of them, the i-th
-//   longest and the i-th shortest, back to back.  Dense launches run it on
-//   16x16x32 MFMAs, block-sparse and (192, 128) ones on 32x32x16.
+//   longest and the i-th shortest, back to back.  d = 128 launches (dense
+//   and block-sparse) run it on 16x16x32 MFMAs, (192, 128) ones on 32x32x16.
 // * d = 64: attn_fwd_kernel, 4 waves / 128 query rows per workgroup, each
 //   wave interleaving its own softmax with its MFMAs slice by slice; K/V tiles
 //   move global -> LDS directly (buffer_load ... lds), K two tiles ahead.
@@ -144,9 +145,10 @@ constexpr float kTwoPowTau = 256.0f;  // 2^kTau
 #endif
 constexpr bool kForceSafe = ATTN_FORCE_SAFE != 0;
 
-// The dense d = 128 forward on v_mfma_f32_16x16x32_bf16 (1, the default) or
-// on v_mfma_f32_32x32x16_bf16 (0), the shape the block-sparse and (192, 128)
-// kernels always use: with 16x16x32 they would exceed 256 VGPRs and spill.
+// The d = 128 forward (dense and block-sparse) on v_mfma_f32_16x16x32_bf16
+// (1, the default) or on v_mfma_f32_32x32x16_bf16 (0), the shape the
+// (192, 128) kernel always uses: with 16x16x32 it would exceed 256 VGPRs and
+// spill.
 // Under the chip's power limit the smaller shape holds a higher clock (fewer
 // accumulator registers read per FLOP), at the price of twice as many MFMA
 // issues and row statistics spread over four lanes instead of two.
@@ -1570,10 +1572,10 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (causal)
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, true, false, true>), dim3(wgs),
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, true, false, true, kPpMfma16>), dim3(wgs),
                        dim3(kPpThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, false, false, true>), dim3(wgs),
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 128, false, false, true, kPpMfma16>), dim3(wgs),
                        dim3(kPpThreads), 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -304,8 +304,8 @@ const char* attn_strerror(int status);
  * summary), section 3.1.1, prices the attention tile in cycles of the matrix
  * core; this call measures what that unit sustains on the device under a full
  * grid, with either MFMA shape the forward uses (v_mfma_f32_32x32x16_bf16:
- * the d = 64, (192, 128) and block-sparse kernels; v_mfma_f32_16x16x32_bf16:
- * the dense d = 128 kernel) and no other work, so the forward's rate can be compared
+ * the d = 64 and (192, 128) kernels; v_mfma_f32_16x16x32_bf16: the d = 128
+ * kernel) and no other work, so the forward's rate can be compared
  * with it as well as with the published peak.  The clock drops under
  * matrix-core load by an amount that depends on the operand bits, hence the
  * caller-supplied operands.
