@@ -47,6 +47,10 @@ SMALL = [
     (1, 1, 1, 1, 1, 128, True, False),
     (1, 64, 0, 1, 1, 128, False, False),
     (1, 96, 0, 2, 1, 64, True, False),
+    # d = 128 with more query rows than keys under the causal mask (rows past
+    # Nk see every key), grouped heads, and key padding with it
+    (1, 517, 130, 4, 2, 128, True, False),
+    (2, 300, 200, 8, 4, 128, True, True),
 ]
 
 
