@@ -124,6 +124,30 @@ def make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=1.0, d_v=None):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_trend_qkv(B, N, Hq, Hkv, d, seed, scale, step, jump_at=None, jump=0.0, d_v=None):
+    """Q, K, V whose scores climb (or fall) along the keys, as bf16 CPU tensors.
+
+    Drawn as make_qkv (Q, K, V i.i.d. N(0, 1)), then dimension 0 is replaced:
+    every query row of an even query head holds +8 there and of an odd head
+    -8, and key j holds j * step / (8 |scale|), plus jump / (8 |scale|) at key
+    jump_at.  So scale * q_i . k_j is +-(j * step (+ jump)) up to the sign of
+    scale, plus the N(0, 1)-scale contribution of the other d - 1 dimensions:
+    rows of one parity find a larger maximum in every later key tile (and,
+    past jump_at, one key far above all earlier ones), rows of the other
+    parity keep their maximum in the first keys.  Shapes as make_qkv with
+    Nq = Nk = N.
+    """
+    q, k, v = make_qkv(B, N, N, Hq, Hkv, d, seed, d_v=d_v)
+    q, k = q.float(), k.float()
+    sign = torch.tensor([1.0 if h % 2 == 0 else -1.0 for h in range(Hq)])
+    q[..., 0] = 8.0 * sign
+    t = torch.arange(N, dtype=torch.float32) * float(step)
+    if jump_at is not None:
+        t[jump_at] += float(jump)
+    k[..., 0] = (t / (8.0 * abs(scale)))[None, :, None]
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v
+
+
 def make_dout(shape, seed):
     """Upstream gradient dO of the given shape: i.i.d. N(0,1) rounded once to bf16."""
     g = torch.Generator().manual_seed(int(seed))

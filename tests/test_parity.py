@@ -3,7 +3,9 @@
 Small shapes are compared element by element over every output; they span
 several query and key tiles, ragged tails, Nq != Nk, every GQA group size of
 the workloads, key padding (including empty and full rows) and packed
-sequences.  The full-size workloads are launched exactly as the benchmark
+sequences; inputs whose scores climb along the keys drive the conditional
+rescale at every key tile and overflow exponentials taken against a stale
+maximum.  The full-size workloads are launched exactly as the benchmark
 launches them, into outputs prefilled with NaN, and compared with the oracle
 on every element, plus properties that hold at any size (the GPU's own LSE
 normalises its row, reruns are bitwise identical, nothing outside the outputs
@@ -414,6 +416,68 @@ def test_any_finite_scale_other_entry_points():
         o_ref, lse_ref = oracle.attention_forward_blocksparse(to_np64(q), to_np64(k), to_np64(v),
                                                               scale, bm.numpy(), 128, 128, False)
         assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), f"sparse scale {scale}")
+
+
+# ------------------------------------------------------------------ scores that climb along the keys
+
+# Score step 0.25 per key (23 log2 units per 64-key tile) and, at key 400, one
+# key 100 above the trend (144 log2 units): rows of even query heads find a
+# maximum more than tau = 8 log2 units above their running one in every key
+# tile up to the jump, and exponentials taken against their stale maximum
+# overflow to +inf there; rows of odd heads keep their first tile's maximum
+# and the later tiles' exponentials underflow to 0.  LSE reaches ~200.
+TREND = dict(step=0.25, jump_at=400, jump=100.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_climbing_scores_rescale_every_tile(d, causal, sign):
+    """The conditional rescale at every key tile, and a stale maximum that overflows exp2."""
+    B, N, Hq, Hkv = 2, 600, 4, 2
+    scale = sign / math.sqrt(d)
+    q, k, v = inputs.make_trend_qkv(B, N, Hq, Hkv, d, 9400 + d, scale, **TREND)
+    print(f"[parity] climbing scores d={d} causal={causal} scale={scale:.4f}", flush=True)
+    o, lse = _run(q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.attention_forward(to_np64(q), to_np64(k), to_np64(v), scale, causal,
+                                              workers=8)
+    assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "climbing scores")
+
+
+def test_climbing_scores_other_entry_points():
+    """The same inputs through the (192, 128), block-sparse and packed entry points."""
+    scale = 1.0 / math.sqrt(192)
+    q, k, v = inputs.make_trend_qkv(2, 600, 4, 2, 192, 9410, scale, d_v=128, **TREND)
+    print("[parity] climbing scores (192, 128)", flush=True)
+    for causal in (False, True):
+        o, lse = _run(q, k, v, scale, causal)
+        o_ref, lse_ref = oracle.attention_forward(to_np64(q), to_np64(k), to_np64(v), scale,
+                                                  causal, workers=8)
+        assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "(192,128) climbing")
+
+    scale = 1.0 / math.sqrt(128)
+    q, k, v = inputs.make_trend_qkv(1, 600, 4, 2, 128, 9411, scale, **TREND)
+    g = torch.Generator().manual_seed(9412)
+    bm = (torch.rand((1, 5, 5), generator=g) < 0.6).to(torch.uint8)
+    bm[0, :, 3] = 1  # the block holding the jump
+    print("[parity] climbing scores block-sparse", flush=True)
+    o, lse = attn.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), bm.to(DEV), scale, False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward_blocksparse(to_np64(q), to_np64(k), to_np64(v), scale,
+                                                          bm.numpy(), 128, 128, False)
+    assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "sparse climbing")
+
+    # one packed sequence of 600 rows beside a short one
+    q2, k2, v2 = inputs.make_trend_qkv(1, 130, 4, 2, 128, 9413, scale, step=0.25)
+    qp, kp, vp = (torch.cat([a[0], b[0]]) for a, b in ((q, q2), (k, k2), (v, v2)))
+    cu = inputs.cu_from_lengths([600, 130])
+    print("[parity] climbing scores packed", flush=True)
+    o, lse = attn.attn_fwd_varlen(qp.to(DEV), kp.to(DEV), vp.to(DEV), cu.to(DEV), cu.to(DEV), 600,
+                                  600, scale, True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward_varlen(to_np64(qp), to_np64(kp), to_np64(vp),
+                                                     cu.numpy(), cu.numpy(), scale, True)
+    assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "packed climbing")
 
 
 # ------------------------------------------------------------------ full-size workloads

@@ -9,7 +9,8 @@ headline benchmark's size and at the d = 64 batch workload's, one whole
 compared element by element.  The packed (varlen) entry point is checked on
 small ragged batches in full (with a zero-length sequence, lq != lk, GQA and
 both masks) and, at the ragged benchmark's size, on its shortest sequence.
-Tolerances are derived in parity_util.
+Tolerances are derived in parity_util (and, for a dQ column that is a small
+difference of large terms, in the climbing-score test).
 """
 
 import math
@@ -142,6 +143,55 @@ def test_backward_any_finite_scale_full_oracle(d, scale_mult):
                 assert np.abs(ref).max() == 0.0, name
                 continue
             assert_grad_parity(grad_errors(to_np64(got), ref), name)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_climbing_scores_full_oracle(d, causal):
+    """Scores that climb along the keys (a new row maximum in every key tile, one
+    key 100 above the trend) or fall (later tiles' P underflows): the forward
+    rescales at every tile, and the backward rebuilds P from an LSE near 200.
+
+    The trend lives in dimension 0 of the keys (up to ~300 there, against
+    N(0, 1) elsewhere).  Since sum_j dS_ij = 0, dQ_i0 = scale sum_j dS_ij K_j0
+    is the small difference of terms as large as scale sum_j |dS_ij| |K_j0|:
+    rounding dS to bf16 (<= 2^-9 relative) and D = <dO, O> taken from the
+    bf16 O (<= 2^-9 sum_d |dO_id O_id|) move it by up to 2^-9 scale
+    sum_j (|dS_ij| + P_ij sum_d |dO_id O_id|) |K_j0|, whatever the kernel
+    (a CPU model of those two roundings alone reaches 0.55 of this).  That
+    column is held to twice this bound plus its own bf16 rounding; every
+    other column of dQ, and dK and dV, to the usual bars.
+    """
+    B, N, Hq, Hkv = 1, 600, 4, 2
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = inputs.make_trend_qkv(B, N, Hq, Hkv, d, 9420 + d, scale, step=0.25, jump_at=400,
+                                    jump=100.0)
+    do = inputs.make_dout(q.shape, 9421 + d)
+    print(f"[parity-bwd] climbing scores d={d} causal={causal}", flush=True)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, scale, causal, None)
+    qn, kn, vn, don = (to_np64(t) for t in (q, k, v, do))
+    rq, rk, rv = oracle.attention_backward(qn, kn, vn, don, scale, causal, None, workers=8)
+    dqn = to_np64(dq)
+    for name, got, ref in (("dq[..., 1:]", dqn[..., 1:], rq[..., 1:]), ("dk", to_np64(dk), rk),
+                           ("dv", to_np64(dv), rv)):
+        errs = grad_errors(got, ref)
+        print(f"[parity-bwd]   {name}: {errs}", flush=True)
+        assert_grad_parity(errs, name)
+    worst = 0.0
+    for h in range(Hq):
+        kh = kn[0, :, h // (Hq // Hkv)]
+        _, _, _, p, ds = oracle.attention_backward_head(qn[0, :, h], kh, vn[0, :, h // (Hq // Hkv)],
+                                                        don[0, :, h], scale, causal,
+                                                        return_ds=True)
+        o_bf = (p @ vn[0, :, h // (Hq // Hkv)]).astype(np.float32)
+        o_bf = torch.from_numpy(o_bf).to(torch.bfloat16).double().numpy()
+        d_err = np.abs(o_bf * don[0, :, h]).sum(axis=1, keepdims=True)
+        bound = 2.0 ** -9 * scale * ((np.abs(ds) + p * d_err) @ np.abs(kh[:, 0]))
+        err = np.abs(dqn[0, :, h, 0] - rq[0, :, h, 0])
+        allowed = np.maximum(2 * bound + 2.0 ** -8 * np.abs(rq[0, :, h, 0]), 1e-30)
+        worst = max(worst, float((err / allowed).max()))
+    print(f"[parity-bwd]   dq[..., 0]: error / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
 
 
 @pytest.mark.parametrize("d", [128, 64])
