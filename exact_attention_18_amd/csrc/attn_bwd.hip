@@ -937,9 +937,8 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
       (need_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))))
     return ATTN_ERR_ALIGN;
   const long rows = (long)B * Nq * Hq;
-  if (rows > INT_MAX || (long)B * Nk * Hkv > INT_MAX || (long)Nq * Hq * d > INT_MAX / 2 ||
-      (long)Nk * Hkv * d > INT_MAX / 2)
-    return ATTN_ERR_TOO_LARGE;
+  // Row counts stay within int; element offsets are 64-bit throughout.
+  if (rows > INT_MAX || (long)B * Nk * Hkv > INT_MAX) return ATTN_ERR_TOO_LARGE;
   return ATTN_OK;
 }
 

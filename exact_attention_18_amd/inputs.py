@@ -124,6 +124,21 @@ def make_qkv(B, Nq, Nk, Hq, Hkv, d, seed, q_mult=1.0, d_v=None):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_qkv_on(device, B, Nq, Nk, Hq, Hkv, d, seed):
+    """As make_qkv (Q, K, V i.i.d. N(0, 1), rounded once to bf16), drawn on `device`.
+
+    For inputs of several GiB, which the host would take long to draw: a
+    seeded generator of that device fills them there, and a checker reads the
+    very tensors back.
+    """
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    out = []
+    for shape in ((B, Nq, Hq, d), (B, Nk, Hkv, d), (B, Nk, Hkv, d)):
+        out.append(torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+                   .to(torch.bfloat16))
+    return tuple(out)
+
+
 def make_trend_qkv(B, N, Hq, Hkv, d, seed, scale, step, jump_at=None, jump=0.0, d_v=None):
     """Q, K, V whose scores climb (or fall) along the keys, as bf16 CPU tensors.
 

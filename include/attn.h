@@ -93,7 +93,8 @@ enum attn_status {
  *   seqlens_k : NULL, or device int32 [B] of valid key counts per batch
  *               element (key padding); shared by all heads.
  *   stream    : hipStream_t to launch on (NULL: default stream).
- * Returns an attn_status.
+ * Returns an attn_status (ATTN_ERR_TOO_LARGE when B * Nq or B * Nk exceeds
+ * 2^31 - 1; element offsets are 64-bit, so arrays may exceed 4 GiB).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
@@ -220,7 +221,8 @@ int attn_varlen_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, i
  * Results are deterministic: every dQ row is summed inside one workgroup and
  * every dK / dV row likewise, with no atomic adds.  Asynchronous on stream;
  * allocates nothing.  Returns an attn_status (ATTN_ERR_HEAD_DIM for d not 64 or 128;
- * ATTN_ERR_NULL / ATTN_ERR_ALIGN as for attn_fwd, including the workspace).
+ * ATTN_ERR_NULL / ATTN_ERR_ALIGN as for attn_fwd, including the workspace;
+ * ATTN_ERR_TOO_LARGE when B * Nq * Hq or B * Nk * Hkv exceeds 2^31 - 1).
  * B == 0, or Nq == 0 and Nk == 0, is a no-op.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

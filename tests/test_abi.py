@@ -251,6 +251,8 @@ def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv
     (dict(dq=FAKE + 2), attn.ATTN_ERR_ALIGN),
     (dict(dv=FAKE + 4), attn.ATTN_ERR_ALIGN),
     (dict(lse=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(B=1 << 20, Hq=1024, Hkv=1, Nq=1024), attn.ATTN_ERR_TOO_LARGE),  # query rows x heads
+    (dict(B=1 << 16, Hq=1, Hkv=1, Nq=1, Nk=1 << 16), attn.ATTN_ERR_TOO_LARGE),  # key rows x heads
 ])
 def test_attn_bwd_rejects_bad_arguments(kw, code):
     assert _bwd(**kw) == code

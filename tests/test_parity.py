@@ -480,6 +480,33 @@ def test_climbing_scores_other_entry_points():
     assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "packed climbing")
 
 
+# ------------------------------------------------------------------ key rows past 2 GiB
+
+@pytest.mark.parametrize("d,padded", [(128, False), (64, True)])
+def test_key_rows_past_2gib(d, padded):
+    """K and V of 2^18 + 77 rows of 8 KiB (4096 / d KV heads): rows past 2 GiB
+    into each array, so every key address needs more than 31 bits.  Short
+    query blocks see every key (non-causal); the first and the last head are
+    compared with the oracle on every row."""
+    B, Nq, Nk = 1, 100, (1 << 18) + 77
+    H = 8192 // (2 * d)
+    q, k, v = inputs.make_qkv_on(DEV, B, Nq, Nk, H, H, d, 9500 + d)
+    assert k[0, -1].data_ptr() - k.data_ptr() > 2 ** 31
+    seqlens = torch.tensor([Nk - 5], dtype=torch.int32) if padded else None
+    scale = 1.0 / math.sqrt(d)
+    print(f"[parity] key rows past 2 GiB d={d} H={H} Nk={Nk} padded={padded}", flush=True)
+    o, lse = _run(q, k, v, scale, False, seqlens)
+    nk = Nk - 5 if padded else Nk
+    for h in (0, H - 1):
+        o_ref, lse_ref = oracle.attention_forward(
+            to_np64(q[:, :, h:h + 1]), to_np64(k[:, :nk, h:h + 1]), to_np64(v[:, :nk, h:h + 1]),
+            scale, False)
+        assert_parity(errors(to_np64(o[:, :, h:h + 1]), to_np64(lse[:, h:h + 1]), o_ref, lse_ref),
+                      f"head {h}")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = [name for name in inputs.WORKLOADS if name != "single_head_n256_d64"]

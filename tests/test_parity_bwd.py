@@ -195,6 +195,32 @@ def test_backward_climbing_scores_full_oracle(d, causal):
 
 
 @pytest.mark.parametrize("d", [128, 64])
+def test_backward_key_rows_past_2gib(d):
+    """The backward over K and V of 2^18 + 77 rows of 8 KiB (4096 / d KV heads):
+    rows past 2 GiB into each array.  dQ, dK and dV of heads 0 and the last
+    against the oracle in full."""
+    B, Nq, Nk = 1, 100, (1 << 18) + 77
+    H = 8192 // (2 * d)
+    q, k, v = inputs.make_qkv_on(DEV, B, Nq, Nk, H, H, d, 9510 + d)
+    do = inputs.make_dout(q.shape, 9511 + d).to(DEV)
+    assert k[0, -1].data_ptr() - k.data_ptr() > 2 ** 31
+    scale = 1.0 / math.sqrt(d)
+    print(f"[parity-bwd] key rows past 2 GiB d={d} H={H} Nk={Nk}", flush=True)
+    o, lse = attn.attn_fwd(q, k, v, scale, False)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, lse, do, scale, False)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        rq, rk, rv = oracle.attention_backward_head(to_np64(q[0, :, h]), to_np64(k[0, :, h]),
+                                                    to_np64(v[0, :, h]), to_np64(do[0, :, h]),
+                                                    scale, False)
+        for name, got, ref in (("dq", dq[0, :, h], rq), ("dk", dk[0, :, h], rk),
+                               ("dv", dv[0, :, h], rv)):
+            assert_grad_parity(grad_errors(to_np64(got), ref), f"{name} head {h}")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d", [128, 64])
 def test_backward_is_deterministic(d):
     q, k, v = inputs.make_qkv(2, 700, 700, 8, 2, d, 9100, q_mult=3.0)
     do = inputs.make_dout(q.shape, 9101)
