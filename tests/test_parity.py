@@ -172,6 +172,26 @@ def test_blocksparse_full_oracle(B, Nq, Nk, Hq, Hkv, causal, padded, mh, density
     assert np.isneginf(to_np64(lse)[empty]).all()
 
 
+def test_blocksparse_longest_key_range():
+    """Block-sparse at its largest key range, Nk = 262144 (4096 key tiles of 64):
+    one query block visits every tile (its work list full), the other a random
+    half of the blocks; all rows against the oracle."""
+    Nq, Nk = 256, 262144
+    q, k, v = inputs.make_qkv(1, Nq, Nk, 1, 1, 128, 7900, q_mult=2.0)
+    nbk = Nk // 128
+    g = torch.Generator().manual_seed(7901)
+    bm = torch.zeros((1, Nq // 128, nbk), dtype=torch.uint8)
+    bm[0, 0] = 1
+    bm[0, 1] = (torch.rand(nbk, generator=g) < 0.5).to(torch.uint8)
+    scale = 1.0 / math.sqrt(128)
+    print(f"[parity] block-sparse Nk={Nk}", flush=True)
+    o, lse = attn.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), bm.to(DEV), scale, False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward_blocksparse(
+        to_np64(q), to_np64(k), to_np64(v), scale, bm.numpy(), 128, 128, False, workers=8)
+    assert_parity(errors(to_np64(o), to_np64(lse), o_ref, lse_ref), "block-sparse Nk=262144")
+
+
 def test_blocksparse_all_ones_is_the_dense_kernel_bitwise():
     """With every block set, the block-sparse kernel visits every key tile in order, as the dense one.
 
