@@ -360,6 +360,29 @@ def test_grouped_heads_equal_repeated_kv_heads_bitwise_varlen():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("d_qk,d_v", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values_give_constant_output(d_qk, d_v, causal):
+    """V equal to a constant c_h in every row of KV head h: every row with a
+    visible key gets O = c_h exactly in real arithmetic (its weights sum to
+    one), whatever the scores.  On peaky rows (Q x 3) the GPU's O differs from
+    c_h only by the bf16 rounding of P against the fp32 row sum (at most 2^-9
+    relative) and of O itself (one bf16 step at 1.5 is 2^-7)."""
+    B, N, Hq, Hkv = 2, 333, 4, 2
+    q, k, _ = inputs.make_qkv(B, N, N, Hq, Hkv, d_qk, 9600 + d_qk + int(causal), q_mult=3.0)
+    consts = torch.tensor([1.5, -0.375], dtype=torch.bfloat16)  # exact in bf16
+    v = consts.view(1, 1, Hkv, 1).expand(B, N, Hkv, d_v).contiguous()
+    scale = 1.0 / math.sqrt(d_qk)
+    print(f"[parity] constant V d=({d_qk},{d_v}) causal={causal}", flush=True)
+    o, lse = _run(q, k, v, scale, causal)
+    want = consts.float().repeat_interleave(Hq // Hkv).view(1, 1, Hq, 1).double().numpy()
+    err = np.abs(to_np64(o) - want)
+    assert err.max() <= 2.0 ** -7 + 2.0 ** -9 * 1.5, err.max()
+    _, lse_ref = oracle.attention_forward(to_np64(q), to_np64(k), to_np64(v), scale, causal,
+                                          workers=8)
+    assert np.abs(to_np64(lse) - lse_ref).max() <= 1e-3
+
+
 def test_key_shift_moves_lse_by_the_query_dot_shift():
     """softmax(x) = softmax(x - c): adding w to every key moves LSE_i by scale*q_i.w."""
     B, N, H, d = 1, 300, 2, 64
