@@ -195,6 +195,41 @@ def test_backward_climbing_scores_full_oracle(d, causal):
 
 
 @pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_constant_values_give_zero_score_gradients(d, causal):
+    """With V equal to a constant c_h in every row of KV head h, O = c_h for any
+    scores, so dQ = dK = 0 exactly: dP_ij = c_h sum_d dO_id equals D_i = <dO_i,
+    O_i> and dS = P (dP - D) vanishes.  The GPU forms D from its bf16 O, so
+    dS_ij is P_ij times at most |sum_d dO_id (O_id - c_h)| plus fp32 rounding,
+    which bounds dQ_i by scale e_i max|K| and dK_j by scale sum_i P_ij e_i |Q_i|
+    (e_i that residue, P_ij <= 1).  dV = P^T dO is compared with the oracle."""
+    B, N, Hq, Hkv = 1, 333, 4, 2
+    q, k, _ = inputs.make_qkv(B, N, N, Hq, Hkv, d, 9700 + d + int(causal), q_mult=3.0)
+    consts = torch.tensor([1.5, -0.375], dtype=torch.bfloat16)
+    v = consts.view(1, 1, Hkv, 1).expand(B, N, Hkv, d).contiguous()
+    do = inputs.make_dout(q.shape, 9701 + d)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[parity-bwd] constant V d={d} causal={causal}", flush=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = attn.attn_fwd(qd, kd, vd, scale, causal)
+    dq, dk, dv = attn.attn_bwd(qd, kd, vd, o, lse, dod, scale, causal)
+    torch.cuda.synchronize()
+    qn, kn, don, on = to_np64(q), to_np64(k), to_np64(do), to_np64(o)
+    c = np.repeat(consts.double().numpy(), Hq // Hkv)                   # per query head
+    absdo = np.abs(don).sum(axis=-1)                                    # [B, N, Hq]
+    e = np.abs((don * (on - c[None, None, :, None])).sum(axis=-1)) + 2.0 ** -20 * np.abs(c) * absdo
+    dq_bound = 2 * scale * e * np.abs(kn).max() + 1e-30
+    assert (np.abs(to_np64(dq)).max(axis=-1) <= dq_bound).all()
+    G = Hq // Hkv
+    dkn = to_np64(dk)
+    for g in range(Hkv):  # a KV head's dK sums its G query heads
+        dk_bound = 2 * scale * e[:, :, g * G:(g + 1) * G].sum() * np.abs(qn).max() + 1e-30
+        assert np.abs(dkn[:, :, g]).max() <= dk_bound
+    _, _, rv = oracle.attention_backward(qn, kn, to_np64(v), don, scale, causal, None, workers=8)
+    assert_grad_parity(grad_errors(to_np64(dv), rv), "dv")
+
+
+@pytest.mark.parametrize("d", [128, 64])
 def test_backward_key_rows_past_2gib(d):
     """The backward over K and V of 2^18 + 77 rows of 8 KiB (4096 / d KV heads):
     rows past 2 GiB into each array.  dQ, dK and dV of heads 0 and the last
