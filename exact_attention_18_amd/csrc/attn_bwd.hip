@@ -60,6 +60,16 @@
 
 namespace {
 
+// Race check (as in the forward): a library built with -DATTN_FORCE_SAFE=1
+// keeps every arithmetic step and its order, but the two wave groups of both
+// ping-pong kernels run in lockstep instead of half a period apart, and every
+// workgroup barrier waits first for all of the wave's outstanding memory
+// operations.  Its gradients must equal the tuned build's bit for bit.
+#ifndef ATTN_FORCE_SAFE
+#define ATTN_FORCE_SAFE 0
+#endif
+constexpr bool kForceSafe = ATTN_FORCE_SAFE != 0;
+
 // Head dimensions D of the backward kernels: 64 and 128.
 constexpr int kBwThreads = 256;         // 4 waves
 constexpr int kKeysPerWg = 128;         // dK/dV kernel: keys per workgroup
@@ -381,6 +391,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     };
     auto barrier = [&]() {
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kForceSafe) __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -491,14 +502,14 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __syncthreads();
-    if (grp == 1) barrier();  // group 1 runs half a period behind
+    if (!kForceSafe && grp == 1) barrier();  // group 1 runs half a period behind
     int i = 0;
     for (; i + 1 < n_per; i += 2) {
       period(i, std::integral_constant<int, 0>{});
       period(i + 1, std::integral_constant<int, 1>{});
     }
     if (i < n_per) period(i, std::integral_constant<int, 0>{});
-    if (grp == 0) barrier();
+    if (!kForceSafe && grp == 0) barrier();
     __syncthreads();
 
     // ---- combine: group 1's partial sums go through LDS (fp32, [key][d]) into group 0's
@@ -685,6 +696,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     auto vbuf = [&](auto I) -> __bf16* { return v_t[decltype(I)::value & 1]; };
     auto barrier = [&]() {
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kForceSafe) __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -784,7 +796,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     if (n_tiles > 1) fetch(1);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __syncthreads();
-    if (grp == 1) barrier();  // group 1 runs half a period behind
+    if (!kForceSafe && grp == 1) barrier();  // group 1 runs half a period behind
     int j = 0;
     for (; j + 3 <= n_tiles; j += 4) {
       period(j, std::integral_constant<int, 0>{});
@@ -795,7 +807,7 @@ __global__ __launch_bounds__(kBwPpThreads, 1) void bwd_dq_pp_kernel(BwdParams p)
     if (j <= n_tiles) period(j, std::integral_constant<int, 0>{});
     if (j + 1 <= n_tiles) period(j + 1, std::integral_constant<int, 1>{});
     if (j + 2 <= n_tiles) period(j + 2, std::integral_constant<int, 2>{});
-    if (grp == 0) barrier();
+    if (!kForceSafe && grp == 0) barrier();
 
     // dQ leaves through LDS: a lane's accumulator holds 4-column pieces of one
     // row, so storing it directly scatters every store instruction over 32

@@ -9,7 +9,9 @@ the tuned build points at a missing wait or barrier there.  The cases cover
 the headline workload at full size (paired work items, four query heads per
 workgroup), a small paired grid, the unpaired d = 64 kernel with key padding,
 the packed form with its LPT order, the block-sparse tile list and the
-(192, 128) head dimensions.
+(192, 128) head dimensions.  The backward's dK/dV and dQ kernels get the same
+treatment (groups in lockstep, every barrier after a full wait), on paired
+and packed grids, at d = 64 and 128, and at the headline's size.
 """
 
 import os
@@ -85,3 +87,40 @@ def test_safe_build_matches_tuned_headline_full_size():
     qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
     print(f"[race] {w.name}", flush=True)
     _assert_same(*_both(lambda: attn.attn_fwd(qd, kd, vd, w.scale, w.causal)))
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,d,causal,padded", [
+    (2, 1000, 8, 2, 128, True, False),   # paired dK/dV and dQ items, 4 heads per dQ workgroup
+    (1, 700, 16, 2, 128, False, True),   # 8 heads per dQ workgroup, key padding
+    (4, 517, 4, 4, 64, True, False),     # d = 64
+])
+def test_safe_build_matches_tuned_backward(B, N, Hq, Hkv, d, causal, padded):
+    """The backward's two ping-pong kernels in lockstep with full waits give the same bits."""
+    q, k, v = inputs.make_qkv(B, N, N, Hq, Hkv, d, 9620 + N + d, q_mult=3.0)
+    do = inputs.make_dout(q.shape, 9621 + N)
+    sl = inputs.make_seqlens(B, N // 3, N, 9622).to(DEV) if padded else None
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = attn.attn_fwd(qd, kd, vd, 0.09, causal, sl)
+    print(f"[race] backward B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal}", flush=True)
+    _assert_same(*_both(lambda: attn.attn_bwd(qd, kd, vd, o, lse, dod, 0.09, causal, sl)))
+
+
+def test_safe_build_matches_tuned_backward_packed_and_headline():
+    lengths = torch.tensor([700, 1, 257, 0, 1500, 64], dtype=torch.int32)
+    cu = inputs.cu_from_lengths(lengths).to(DEV)
+    T, mx = int(lengths.sum()), int(lengths.max())
+    q, k, v = inputs.make_packed_qkv(T, T, 8, 2, 128, 9630, q_mult=3.0)
+    do = inputs.make_dout(q.shape, 9631)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = attn.attn_fwd_varlen(qd, kd, vd, cu, cu, mx, mx, 0.09, True)
+    print("[race] backward packed", flush=True)
+    _assert_same(*_both(lambda: attn.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cu, cu, mx, mx,
+                                                     0.09, True)))
+
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    x = inputs.workload_inputs(w)
+    qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    dod = inputs.make_dout(qd.shape, 9632).to(DEV)
+    o, lse = attn.attn_fwd(qd, kd, vd, w.scale, w.causal)
+    print(f"[race] backward {w.name}", flush=True)
+    _assert_same(*_both(lambda: attn.attn_bwd(qd, kd, vd, o, lse, dod, w.scale, w.causal)))
