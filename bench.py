@@ -25,6 +25,10 @@ mfma_sustained: what the matrix cores sustain on this device with one MFMA
 cpu_baseline: the CPU oracle as it stands, timed on this host on a bounded
               sample of heads of the same workload (heads are independent and
               equal in cost, so the rate is the workload's rate).
+parity_sample: the heads that sample computed, compared element by element
+              with the timed launches' own O and LSE: max and mean |O - O_oracle|
+              and max |LSE - LSE_oracle| (the parity tests' bars are 2e-2, 2e-3
+              and 1e-3).
 """
 
 from __future__ import annotations
@@ -154,7 +158,7 @@ def make_step(w, x, dev):
     return step
 
 
-def cpu_baseline(w, x, target_s: float):
+def cpu_baseline(w, x, target_s: float, got=None):
     """Time the oracle on whole heads until about target_s seconds have passed.
 
     A head is a (batch, query head) pair, or a (sequence, query head) pair of a
@@ -163,6 +167,10 @@ def cpu_baseline(w, x, target_s: float):
     block-sparse workload).  Heads are visited in a seeded random order and
     run `workers` at a time; the rate is the visited heads' algorithmic FLOPs
     over the wall time.
+
+    got: the GPU's (O, LSE) of the workload as float NumPy arrays, or None.
+    Each visited head's oracle result is then compared with its slice of
+    them; returns (baseline, parity) with parity None when got is None.
     """
     from concurrent.futures import ThreadPoolExecutor
 
@@ -175,6 +183,17 @@ def cpu_baseline(w, x, target_s: float):
     v = x["v"].float().numpy()
     G = w.Hq // w.Hkv
     rng = np.random.default_rng(w.seed)
+
+    def diff(o_ref, l_ref, o_got, l_got):
+        """max and sum of |O - O_ref|, element count, max |LSE - LSE_ref| of one head."""
+        if got is None:
+            return None
+        e = np.abs(o_got - o_ref)
+        both_inf = np.isneginf(l_got) & np.isneginf(l_ref)
+        de = np.where(both_inf, 0.0, np.abs(l_got - np.where(both_inf, 0.0, l_ref)))
+        return (float(e.max()) if e.size else 0.0, float(e.sum()), e.size,
+                float(de.max()) if de.size else 0.0)
+
     if w.varlen:
         cu = x["cu_seqlens_q"].numpy()
         heads = [(z, h) for z in range(len(cu) - 1) for h in range(w.Hq)]
@@ -182,10 +201,12 @@ def cpu_baseline(w, x, target_s: float):
         def one(zh):
             z, h = zh
             a, e = int(cu[z]), int(cu[z + 1])
-            oracle.attention_head(q[a:e, h], k[a:e, h // G], v[a:e, h // G], w.scale, w.causal)
+            o_ref, l_ref = oracle.attention_head(q[a:e, h], k[a:e, h // G], v[a:e, h // G],
+                                                 w.scale, w.causal)
             L = e - a
             f = 2.0 * L * L * (w.d + w.d_v)
-            return f / 2.0 if w.causal else f
+            cmp = None if got is None else diff(o_ref, l_ref, got[0][a:e, h], got[1][h, a:e])
+            return (f / 2.0 if w.causal else f), cmp
     else:
         sl = None if x.get("seqlens_k") is None else x["seqlens_k"].numpy()
         allowed = None
@@ -198,31 +219,42 @@ def cpu_baseline(w, x, target_s: float):
         def one(bh):
             b, h = bh
             nk = None if sl is None else int(sl[b])
-            oracle.attention_head(q[b, :, h], k[b, :, h // G], v[b, :, h // G], w.scale, w.causal,
-                                  nk, allowed=allowed)
-            return per_head
+            o_ref, l_ref = oracle.attention_head(q[b, :, h], k[b, :, h // G], v[b, :, h // G],
+                                                 w.scale, w.causal, nk, allowed=allowed)
+            cmp = None if got is None else diff(o_ref, l_ref, got[0][b, :, h], got[1][b, h])
+            return per_head, cmp
     rng.shuffle(heads)
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover - threadpoolctl is present in this image
         threadpool_limits = None
     done, flop, t_total, pos = 0, 0.0, 0.0, 0
+    cmps = []
     with ThreadPoolExecutor(max_workers=workers) as ex:
         while pos < len(heads) and t_total < target_s:
             chunk = heads[pos:pos + workers]
             t0 = time.perf_counter()
             if threadpool_limits is not None:
                 with threadpool_limits(limits=1):
-                    flop += sum(ex.map(one, chunk))
+                    res = list(ex.map(one, chunk))
             else:
-                flop += sum(ex.map(one, chunk))
+                res = list(ex.map(one, chunk))
             t_total += time.perf_counter() - t0
+            flop += sum(r[0] for r in res)
+            cmps += [r[1] for r in res if r[1] is not None]
             done += len(chunk)
             pos += len(chunk)
     kind = "(sequence, head)" if w.varlen else "(batch, head)"
-    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+    base = {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"{done} of {len(heads)} {kind} pairs of {w.name}, fp64 NumPy with S and P "
                       f"materialised, {workers} threads, {t_total:.1f} s wall"}
+    parity = None
+    if got is not None:
+        n = sum(c[2] for c in cmps)
+        parity = {"heads": len(cmps), "o_max_abs": max((c[0] for c in cmps), default=0.0),
+                  "o_mean_abs": sum(c[1] for c in cmps) / n if n else 0.0,
+                  "lse_max_abs": max((c[3] for c in cmps), default=0.0)}
+    return base, parity
 
 
 def mfma_sustained(dev, iters: int = 8192, reps: int = 3, seed: int = 7):
@@ -509,7 +541,7 @@ def main():
     t_start.record()
     for i in range(K):
         ev_s[i].record()
-        step()
+        step_out = step()
         ev_e[i].record()
     t_end.record()
     torch.cuda.synchronize()
@@ -532,10 +564,12 @@ def main():
         probe["forward_mfma_shape"] = "16x16x32" if shape16 else "32x32x16"
         ref = probe["shape_16x16x32"]["random"] if shape16 else probe["random"]
         probe["forward_frac_of_random"] = round(achieved / ref["tflops"], 4)
-    cpu = None
+    cpu = parity = None
     if args.cpu_seconds > 0:
+        # the timed launches' own outputs, for the heads the oracle sample computes
+        got = tuple(t.float().cpu().numpy() for t in step_out)
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x, args.cpu_seconds)
+        cpu, parity = cpu_baseline(w, x, args.cpu_seconds, got)
     cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "d_v": w.d_v,
            "causal": w.causal, "q_mult": w.q_mult, "algorithmic_flop": flops,
            "parallelism": "single GPU"}
@@ -564,6 +598,7 @@ def main():
                      "kernel_ms": round(kernel_ms, 5)},
         "mfma_sustained": probe,
         "cpu_baseline": cpu,
+        "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)
 

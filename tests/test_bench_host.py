@@ -1,4 +1,4 @@
-"""CPU: host-side logic of bench.py that decides whether a profile summary applies.
+"""CPU: host-side logic of bench.py: whether a profile summary applies, and the parity sample.
 
 A committed rocprofv3 summary carries the sha256 of the forward's code it was
 taken on; bench.py reports its traffic only while the code is unchanged.
@@ -66,3 +66,28 @@ def test_committed_summaries_describe_the_current_code():
         assert m and m.group(1) == sha, os.path.basename(f)
         w = os.path.basename(f)[len("attn_fwd_"):-len(".md")]
         assert bench.measured_traffic(w) is not None, w
+
+
+def test_parity_sample_compares_the_heads_the_oracle_sample_computes():
+    """cpu_baseline's comparison with the GPU's outputs: zero against the oracle's
+    own result, and a planted error in one element is reported at its size."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_18_amd import inputs
+
+    w = inputs.WORKLOADS["single_head_n256_d64"]
+    x = inputs.workload_inputs(w)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    o, lse = oracle.attention_forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), w.scale, w.causal)
+    base, parity = bench.cpu_baseline(w, x, 5.0, got=(o, lse))
+    assert base["kind"] == "oracle" and parity["heads"] == 1
+    assert parity["o_max_abs"] == 0.0 and parity["lse_max_abs"] == 0.0
+    o2 = o.copy()
+    o2[0, 17, 0, 3] += 0.25
+    lse2 = lse.copy()
+    lse2[0, 0, 5] -= 0.125
+    _, parity = bench.cpu_baseline(w, x, 5.0, got=(o2, lse2))
+    assert abs(parity["o_max_abs"] - 0.25) < 1e-12 and abs(parity["lse_max_abs"] - 0.125) < 1e-12
+    assert abs(parity["o_mean_abs"] - 0.25 / o.size) < 1e-12
+    assert bench.cpu_baseline(w, x, 5.0)[1] is None
