@@ -383,6 +383,36 @@ def test_constant_values_give_constant_output(d_qk, d_v, causal):
     assert np.abs(to_np64(lse) - lse_ref).max() <= 1e-3
 
 
+def test_side_streams_and_concurrent_calls():
+    """Calls on two non-default streams at once (each call runs on the stream
+    current when it is made, shares no state with other calls and allocates
+    nothing) give the default-stream results bit for bit, forward and
+    backward."""
+    cases = []
+    for B, N, Hq, Hkv, d, causal, seed in ((2, 1000, 8, 2, 128, True, 9800),
+                                           (3, 700, 4, 4, 64, False, 9801)):
+        q, k, v = inputs.make_qkv(B, N, N, Hq, Hkv, d, seed, q_mult=2.0)
+        do = inputs.make_dout(q.shape, seed + 1)
+        cases.append(tuple(t.to(DEV) for t in (q, k, v, do)) + (causal,))
+
+    def run(qd, kd, vd, dod, causal):
+        o, lse = attn.attn_fwd(qd, kd, vd, 0.09, causal)
+        return (o, lse) + tuple(attn.attn_bwd(qd, kd, vd, o, lse, dod, 0.09, causal))
+
+    ref = [run(*c) for c in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    got = []
+    for st, c in zip(streams, cases):
+        with torch.cuda.stream(st):
+            got.append(run(*c))
+    torch.cuda.synchronize()
+    print("[parity] two side streams", flush=True)
+    for r, g in zip(ref, got):
+        for x, y in zip(r, g):
+            assert torch.equal(x, y)
+
+
 def test_key_shift_moves_lse_by_the_query_dot_shift():
     """softmax(x) = softmax(x - c): adding w to every key moves LSE_i by scale*q_i.w."""
     B, N, H, d = 1, 300, 2, 64
